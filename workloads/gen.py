@@ -1,0 +1,370 @@
+"""Seeded input recipes for paged-KV verification attention.
+
+Everything here is drawn on the CPU with ``torch.Generator().manual_seed(seed)``
+in one fixed order -- lengths, page-pool permutation, draft-tree parents, Q, K,
+V -- and returned as raw storage arrays (float32 values, bfloat16 bit patterns
+as uint16, OCP e4m3fn codes as uint8), which is exactly what both the GPU
+library and the oracle read.
+
+The layouts follow the paged format of the FlashInfer page "feat: Separate Q
+and KV dtypes for decode" (``begin_forward`` docstring): ``kv_indptr`` counts
+pages per request, ``kv_indices`` lists page ids, ``last_page_len`` is the
+number of filled slots in each request's last page. Query tokens are packed
+varlen by ``qo_indptr`` as in the vLLM page "[Performance] Support MQA/GQA in
+prefill stage by using FlashAttention" (``BlockDiagonalCausalMask.from_seqlens``).
+The draft tokens' own K/V already sit in the cache as each request's last
+``L_b`` positions (vLLM page "[WIP] Support for cached multi-query attention
+towards speculative decoding": all draft keys and values are cached first).
+
+Bit-packed tree masks: request b's ``L_b x L_b`` block, row-major flat index
+``i = t * L_b + j``, bit ``i % 8`` (least significant first) of byte
+``mask_indptr[b] + i // 8``; 1 = token t may attend to draft j. The pages only
+show byte masks (flashmap page ``sglang/verify_attention.py``,
+``_verify_partial_kernel``, the ``USE_MASK`` branch); this packing is the
+build's own layout.
+"""
+
+from __future__ import annotations
+
+import hashlib
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+DTYPES_Q = ("f32", "bf16")
+DTYPES_KV = ("f32", "bf16", "e4m3")
+ELEM_BYTES = {"f32": 4, "bf16": 2, "e4m3": 1}
+E4M3_MAX = 448.0
+NAN_F32 = np.float32("nan")
+NAN_BF16 = np.uint16(0x7FC0)
+NAN_E4M3 = np.uint8(0x7F)
+
+CONFIG_NAMES = {
+    1: "tiny MQA verify fp32 (B2 Hq4 Hkv1 D64, prefix 37/100, L4 causal)",
+    2: "GQA chain verify bf16 (B8 Hq32 Hkv8 D128, prefix 2048, L5 causal)",
+    3: "tree verify bf16 at batch 1 (Hq32 Hkv8 D128, L17 tree, prefix {p})",
+    4: "GQA causal prefill bf16 (B10x1024, Hq64 Hkv8 D128)",
+    5: "mixed-dtype dynamic-draft verify (B64 Hq32 Hkv8 D128, bf16 Q, e4m3 KV, prefix U[512,8192], L U{1..8})",
+}
+
+
+@dataclass
+class Problem:
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    kv_indptr: np.ndarray
+    kv_indices: np.ndarray
+    last_page_len: np.ndarray
+    qo_indptr: np.ndarray
+    mask: Optional[np.ndarray]
+    mask_indptr: Optional[np.ndarray]
+    sm_scale: float
+    k_scale: float
+    v_scale: float
+    q_dtype: str
+    kv_dtype: str
+    max_qo_len: int
+    page_size: int
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+    name: str = ""
+    seed: int = 0
+    info: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return int(self.kv_indptr.shape[0]) - 1
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_cache.shape[0])
+
+
+# ---------------------------------------------------------------- draft trees
+
+
+def chain_parents(length: int) -> np.ndarray:
+    """A draft chain: node i's parent is i - 1 (root 0 has none)."""
+    return np.arange(-1, length - 1, dtype=np.int64)
+
+
+def random_tree_parents(length: int, gen: torch.Generator) -> np.ndarray:
+    """Root 0 plus ``length - 1`` nodes; node i's parent uniform in {0..i-1}."""
+    parents = np.full(length, -1, dtype=np.int64)
+    for i in range(1, length):
+        parents[i] = int(torch.randint(0, i, (1,), generator=gen).item())
+    return parents
+
+
+def tree_mask_rows(parents: Sequence[int]) -> np.ndarray:
+    """Ancestor-or-self relation of a tree given by parent links: ``[L, L]`` bool."""
+    n = len(parents)
+    rows = np.zeros((n, n), dtype=bool)
+    for t in range(n):
+        node = t
+        while node >= 0:
+            rows[t, node] = True
+            node = int(parents[node])
+    return rows
+
+
+def pack_mask_rows(blocks: Sequence[np.ndarray], pad_bytes: int = 0):
+    """Pack per-request ``[L_b, L_b]`` bool blocks into bytes + ``mask_indptr``.
+
+    Row-major, least-significant bit first, each request's segment starting on
+    a byte boundary; ``pad_bytes`` extra zero bytes follow every segment.
+    """
+    segments = []
+    indptr = [0]
+    for blk in blocks:
+        blk = np.asarray(blk, dtype=bool)
+        flat = blk.reshape(-1)
+        nbytes = (flat.size + 7) // 8
+        seg = np.zeros(nbytes + pad_bytes, dtype=np.uint8)
+        for i, bit in enumerate(flat):
+            if bit:
+                seg[i // 8] |= np.uint8(1 << (i % 8))
+        segments.append(seg)
+        indptr.append(indptr[-1] + seg.size)
+    data = np.concatenate(segments) if segments else np.zeros(0, dtype=np.uint8)
+    if data.size == 0:
+        data = np.zeros(1, dtype=np.uint8)
+    return data, np.asarray(indptr, dtype=np.int32)
+
+
+# ---------------------------------------------------------------- storage casts
+
+
+def _to_storage(x: torch.Tensor, dtype: str) -> np.ndarray:
+    """Float32 tensor -> raw storage array in ``dtype`` (RNE casts by torch)."""
+    if dtype == "f32":
+        return x.to(torch.float32).numpy().copy()
+    if dtype == "bf16":
+        return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    if dtype == "e4m3":
+        x = x.clamp(-E4M3_MAX, E4M3_MAX)
+        return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    raise ValueError(dtype)
+
+
+def _nan_code(dtype: str):
+    return {"f32": NAN_F32, "bf16": NAN_BF16, "e4m3": NAN_E4M3}[dtype]
+
+
+def poison_unused(cache: np.ndarray, dtype: str, kv_indptr, kv_indices, last_page_len) -> None:
+    """NaN-fill every slot no request owns: spare pages and last-page tails."""
+    used = np.zeros(cache.shape[0], dtype=bool)
+    nan = _nan_code(dtype)
+    for b in range(len(last_page_len)):
+        pages = kv_indices[kv_indptr[b]:kv_indptr[b + 1]]
+        used[pages] = True
+        if len(pages):
+            cache[pages[-1], int(last_page_len[b]):] = nan
+    cache[~used] = nan
+
+
+# ---------------------------------------------------------------- generic case
+
+
+def make_case(
+    seed: int,
+    *,
+    prefix_lens: Sequence[int],
+    qo_lens: Sequence[int],
+    num_qo_heads: int,
+    num_kv_heads: int,
+    head_dim: int,
+    page_size: int = 16,
+    q_dtype: str = "bf16",
+    kv_dtype: str = "bf16",
+    mask_kind: str = "causal",
+    parents: Optional[Sequence[Sequence[int]]] = None,
+    mask_density: float = 0.5,
+    mask_pad_bytes: int = 0,
+    pool_pages: Optional[int] = None,
+    extra_indices: int = 0,
+    sm_scale: Optional[float] = None,
+    k_scale: float = 1.0,
+    v_scale: float = 1.0,
+    fp8_absmax_scales: bool = False,
+    max_qo_len: Optional[int] = None,
+    poison: bool = True,
+    name: str = "",
+    gen: Optional[torch.Generator] = None,
+) -> Problem:
+    """Build one seeded problem.
+
+    ``mask_kind``: "causal" (no mask array), "chain" (packed chain mask, equal
+    to causal), "tree" (random tree per request unless ``parents`` is given,
+    ancestor-or-self), "random" (independent bits with ``mask_density``; rows
+    may be fully masked), "full" (every bit set).
+    """
+    if q_dtype not in DTYPES_Q or kv_dtype not in DTYPES_KV:
+        raise ValueError((q_dtype, kv_dtype))
+    if num_qo_heads % num_kv_heads:
+        raise ValueError("Hq must be a multiple of Hkv")
+    g = gen if gen is not None else torch.Generator().manual_seed(int(seed))
+    batch = len(prefix_lens)
+    assert len(qo_lens) == batch
+    prefix_lens = [int(x) for x in prefix_lens]
+    qo_lens = [int(x) for x in qo_lens]
+    kv_lens = [p + l for p, l in zip(prefix_lens, qo_lens)]
+    pages_per = [0 if n == 0 else (n + page_size - 1) // page_size for n in kv_lens]
+    last_page_len = np.asarray(
+        [0 if n == 0 else n - (pg - 1) * page_size for n, pg in zip(kv_lens, pages_per)],
+        dtype=np.int32,
+    )
+    needed = int(sum(pages_per))
+    if pool_pages is None:
+        pool_pages = needed + max(8, (needed + 7) // 8)
+    assert pool_pages >= needed
+    perm = torch.randperm(pool_pages, generator=g).numpy().astype(np.int32)
+    kv_indptr = np.zeros(batch + 1, dtype=np.int32)
+    kv_indptr[1:] = np.cumsum(pages_per)
+    kv_indices = np.full(needed + extra_indices, np.int32(0x7FFFFFFF), dtype=np.int32)
+    kv_indices[:needed] = perm[:needed]
+    qo_indptr = np.zeros(batch + 1, dtype=np.int32)
+    qo_indptr[1:] = np.cumsum(qo_lens)
+
+    mask = mask_indptr = None
+    tree_parents = None
+    if mask_kind != "causal":
+        blocks = []
+        tree_parents = []
+        for b in range(batch):
+            L = qo_lens[b]
+            if mask_kind == "chain":
+                par = chain_parents(L)
+                tree_parents.append(par)
+                blocks.append(tree_mask_rows(par))
+            elif mask_kind == "tree":
+                par = (np.asarray(parents[b], dtype=np.int64) if parents is not None
+                       else random_tree_parents(L, g))
+                tree_parents.append(par)
+                blocks.append(tree_mask_rows(par))
+            elif mask_kind == "random":
+                bits = torch.rand((L, L), generator=g).numpy() < mask_density
+                blocks.append(bits)
+            elif mask_kind == "full":
+                blocks.append(np.ones((L, L), dtype=bool))
+            else:
+                raise ValueError(mask_kind)
+        mask, mask_indptr = pack_mask_rows(blocks, pad_bytes=mask_pad_bytes)
+
+    T = int(qo_indptr[-1])
+    q32 = torch.randn((T, num_qo_heads, head_dim), generator=g, dtype=torch.float32)
+    shape = (pool_pages, page_size, num_kv_heads, head_dim)
+    k32 = torch.randn(shape, generator=g, dtype=torch.float32)
+    v32 = torch.randn(shape, generator=g, dtype=torch.float32)
+
+    if fp8_absmax_scales:
+        assert kv_dtype == "e4m3"
+        used = torch.from_numpy(kv_indices[:needed].astype(np.int64))
+        kmax = float(k32[used].abs().max()) if needed else 1.0
+        vmax = float(v32[used].abs().max()) if needed else 1.0
+        k_scale = float(np.float32(kmax / E4M3_MAX))
+        v_scale = float(np.float32(vmax / E4M3_MAX))
+        k32 = k32 / k_scale
+        v32 = v32 / v_scale
+
+    q = _to_storage(q32, q_dtype)
+    k_cache = _to_storage(k32, kv_dtype)
+    v_cache = _to_storage(v32, kv_dtype)
+    del q32, k32, v32
+    if poison:
+        poison_unused(k_cache, kv_dtype, kv_indptr, kv_indices, last_page_len)
+        poison_unused(v_cache, kv_dtype, kv_indptr, kv_indices, last_page_len)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(head_dim)
+    if max_qo_len is None:
+        max_qo_len = max(qo_lens) if qo_lens else 0
+    return Problem(
+        q=q, k_cache=k_cache, v_cache=v_cache,
+        kv_indptr=kv_indptr, kv_indices=kv_indices, last_page_len=last_page_len,
+        qo_indptr=qo_indptr, mask=mask, mask_indptr=mask_indptr,
+        sm_scale=float(np.float32(sm_scale)), k_scale=float(np.float32(k_scale)),
+        v_scale=float(np.float32(v_scale)),
+        q_dtype=q_dtype, kv_dtype=kv_dtype, max_qo_len=int(max_qo_len),
+        page_size=page_size, num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads,
+        head_dim=head_dim, name=name, seed=int(seed),
+        info={"prefix_lens": prefix_lens, "qo_lens": qo_lens, "kv_lens": kv_lens,
+              "parents": tree_parents, "mask_kind": mask_kind},
+    )
+
+
+# ---------------------------------------------------------------- the five workloads
+
+
+def make_config(cid: int, seed: Optional[int] = None, prefix: int = 4096, **overrides) -> Problem:
+    """The five seeded workloads (default seed = config number).
+
+    1: tiny MQA verify, fp32, B 2, Hq 4, Hkv 1, D 64, prefix 37/100, L 4
+       causal, page 16 in a permuted 32-page pool, sm_scale 1/8.
+    2: GQA chain verify, bf16, B 8, Hq 32, Hkv 8, D 128, prefix 2048, L 5 causal.
+    3: tree verify at batch 1, bf16, Hq 32, Hkv 8, D 128, L 17 (root + 16
+       nodes, parent uniform among earlier nodes), ancestor-or-self mask,
+       ``prefix`` in {4096, 16384, 32768}.
+    4: GQA causal prefill, bf16, 10 packed sequences of 1024 tokens, Hq 64,
+       Hkv 8, D 128, prefix 0, K/V in the paged cache.
+    5: bf16 Q with e4m3fn K/V (per-tensor absmax/448 scales), B 64, Hq 32,
+       Hkv 8, D 128, prefix U[512, 8192], L U{1..8} causal, max_qo_len 8.
+    """
+    seed = cid if seed is None else seed
+    if cid == 1:
+        kw = dict(prefix_lens=[37, 100], qo_lens=[4, 4], num_qo_heads=4, num_kv_heads=1,
+                  head_dim=64, q_dtype="f32", kv_dtype="f32", pool_pages=32,
+                  sm_scale=1.0 / 8.0)
+    elif cid == 2:
+        kw = dict(prefix_lens=[2048] * 8, qo_lens=[5] * 8, num_qo_heads=32, num_kv_heads=8,
+                  head_dim=128)
+    elif cid == 3:
+        kw = dict(prefix_lens=[int(prefix)], qo_lens=[17], num_qo_heads=32, num_kv_heads=8,
+                  head_dim=128, mask_kind="tree")
+    elif cid == 4:
+        kw = dict(prefix_lens=[0] * 10, qo_lens=[1024] * 10, num_qo_heads=64,
+                  num_kv_heads=8, head_dim=128)
+    elif cid == 5:
+        g = torch.Generator().manual_seed(int(seed))
+        prefixes = torch.randint(512, 8193, (64,), generator=g).tolist()
+        lens = torch.randint(1, 9, (64,), generator=g).tolist()
+        kw = dict(prefix_lens=prefixes, qo_lens=lens, num_qo_heads=32, num_kv_heads=8,
+                  head_dim=128, q_dtype="bf16", kv_dtype="e4m3", fp8_absmax_scales=True,
+                  max_qo_len=8, gen=g)
+    else:
+        raise ValueError(cid)
+    kw.update(overrides)
+    name = CONFIG_NAMES[cid].format(p=prefix)
+    return make_case(seed, name=name, **kw)
+
+
+# ---------------------------------------------------------------- bookkeeping
+
+
+def problem_sha256(p: Problem) -> str:
+    h = hashlib.sha256()
+    for arr in (p.q, p.k_cache, p.v_cache, p.kv_indptr, p.kv_indices, p.last_page_len,
+                p.qo_indptr):
+        h.update(np.ascontiguousarray(arr).tobytes())
+    if p.mask is not None:
+        h.update(p.mask.tobytes())
+        h.update(p.mask_indptr.tobytes())
+    h.update(np.asarray([p.sm_scale, p.k_scale, p.v_scale], dtype=np.float64).tobytes())
+    return h.hexdigest()
+
+
+def kv_bytes(p: Problem) -> int:
+    """Algorithmic KV bytes: every cached entry of every request, K and V, once per KV head."""
+    kv_lens = np.zeros(p.batch, dtype=np.int64)
+    for b in range(p.batch):
+        pages = int(p.kv_indptr[b + 1] - p.kv_indptr[b])
+        kv_lens[b] = 0 if pages == 0 else (pages - 1) * p.page_size + int(p.last_page_len[b])
+    return int(kv_lens.sum()) * p.num_kv_heads * p.head_dim * 2 * ELEM_BYTES[p.kv_dtype]
