@@ -1,0 +1,179 @@
+/*
+ * verify_attention.h -- C ABI of the MI355X (gfx950) library for multi-query
+ * verification attention over a paged KV cache.
+ *
+ * What one call computes. Each request b has L_b query ("draft") tokens --
+ * a chain or a tree plus its root -- whose keys and values are already the
+ * last L_b entries of the request's paged cache (the vLLM page "[WIP] Support
+ * for cached multi-query attention towards speculative decoding": all draft
+ * keys and values are cached before attention). Query token t of query head
+ * hq attends, with KV head hq / G (G = Hq / Hkv, consecutive query heads
+ * share a KV head: vLLM page "[Performance] Support MQA/GQA in prefill stage
+ * by using FlashAttention"), to
+ *   - every prefix key n < prefix_b = kv_len_b - L_b, and
+ *   - draft key j (key prefix_b + j) iff j <= t (causal, no mask) or iff bit
+ *     (t, j) of the request's bit-packed mask is set (a tree mask in place of
+ *     the causal one: FlashInfer page "How to implement a tree attention with
+ *     flashinfer"),
+ * and returns out = softmax(sm_scale * k_scale * q.K^T) . (v_scale * V) and
+ * lse = natural log of the sum of exp of those scaled logits. The prefix is
+ * split across workgroups and the partial results are merged by their
+ * log-sum-exp (flashmap page "sglang/verify_attention.py",
+ * _verify_partial_kernel / _verify_merge_kernel). A row that sees no key
+ * gets out = 0 and lse = -inf.
+ *
+ * Layouts (dense, row-major, caller-owned DEVICE memory unless noted):
+ *   q, out       [T, Hq, D]        T = qo_indptr[B]; out has q's dtype
+ *   k_cache,
+ *   v_cache      [num_pages, page_size, Hkv, D]   ("NHD" pages)
+ *   kv_indptr    int32 [B + 1]     pages of request b are
+ *   kv_indices   int32 [>= kv_indptr[B]]  kv_indices[kv_indptr[b] .. kv_indptr[b+1])
+ *   last_page_len int32 [B]        entries in request b's last page, 1..page_size
+ *   qo_indptr    int32 [B + 1]     query tokens of request b are rows
+ *                                  qo_indptr[b] .. qo_indptr[b+1] of q
+ *   mask         uint8 [num_mask_bytes] or NULL (NULL = causal)
+ *   mask_indptr  int32 [B + 1] or NULL: byte offset of request b's block
+ *   lse          float32 [T, Hq]
+ * The paged format is the one documented on the FlashInfer page "feat:
+ * Separate Q and KV dtypes for decode" (begin_forward docstring):
+ * kv_len_b = (pages_b - 1) * page_size + last_page_len[b].
+ *
+ * Mask packing (this library's layout): request b's L_b x L_b block,
+ * row-major flat index i = t * L_b + j, bit (i % 8), least significant first,
+ * of byte mask[mask_indptr[b] + i / 8]; 1 = allowed. Each segment must hold
+ * at least ceil(L_b * L_b / 8) bytes.
+ *
+ * Device-content contract (not checked on the host, which never reads device
+ * memory): kv_indptr non-decreasing from 0 with kv_indptr[B] <=
+ * num_kv_indices; 0 <= kv_indices[..] < num_pages; 1 <= last_page_len <=
+ * page_size for requests with pages; qo_indptr non-decreasing from 0 to T;
+ * 0 <= L_b <= min(max_qo_len, kv_len_b); mask segments as above. Kernels
+ * clamp every index they derive from these arrays, so a violation gives
+ * unspecified values but never an out-of-bounds access.
+ *
+ * Calls never allocate, free, synchronise or read device memory on the
+ * host. They enqueue at most two kernels on `stream` (a hipStream_t; NULL =
+ * the default stream) and may be captured into a HIP graph; the workspace
+ * must then outlive the graph. Calls on different streams need different
+ * workspaces. The library keeps only a per-device cache of the compute-unit
+ * count, filled on first use.
+ */
+#ifndef PAGED_KV_VERIFY_ATTENTION_H
+#define PAGED_KV_VERIFY_ATTENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VAT_F32 = 0,        /* IEEE binary32 */
+  VAT_BF16 = 1,       /* bfloat16 */
+  VAT_FP8_E4M3FN = 2  /* OCP FP8 E4M3 (finite-only, max 448): KV cache only */
+} vat_dtype_t;
+
+typedef enum {
+  VAT_OK = 0,
+  VAT_ERR_NULL = 1,        /* a required pointer is NULL */
+  VAT_ERR_SHAPE = 2,       /* inconsistent or negative sizes, Hq % Hkv != 0, bad scales */
+  VAT_ERR_UNSUPPORTED = 3, /* head_dim, page_size, dtype pair or mask length not built */
+  VAT_ERR_ALIGN = 4,       /* q, caches or out not 16-byte aligned */
+  VAT_ERR_WORKSPACE = 5,   /* workspace smaller than vat_workspace_size() */
+  VAT_ERR_HIP = 6          /* the HIP runtime reported an error (device query or launch) */
+} vat_status_t;
+
+/* Shapes and options of one call. Every field is a host integer. */
+typedef struct {
+  int32_t batch;          /* B >= 0 */
+  int32_t num_qo_heads;   /* Hq >= 1 */
+  int32_t num_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;       /* D: 64 or 128 */
+  int32_t page_size;      /* power of two, 1 .. 256 */
+  int32_t num_pages;      /* first dimension of each cache, >= 1 */
+  int32_t num_kv_indices; /* capacity of kv_indices (>= kv_indptr[B]) */
+  int32_t num_qo_tokens;  /* T = rows of q = qo_indptr[B] */
+  int32_t max_qo_len;     /* host bound on every L_b; <= 64 when has_mask */
+  int32_t q_dtype;        /* vat_dtype_t: F32 or BF16; out has this dtype */
+  int32_t kv_dtype;       /* F32 (with F32 q), BF16 or FP8_E4M3FN (with BF16 q) */
+  int32_t has_mask;       /* 0: causal drafts (mask ignored); 1: bit-packed mask */
+  int32_t num_mask_bytes; /* size of mask when has_mask */
+  int32_t num_cus;        /* compute units to plan for; 0 = query the current device */
+  int32_t chunk_keys;     /* -1: planner; 0: no prefix split (one work item per
+                             request, KV head and row block writes out directly);
+                             > 0: prefix chunk length in keys, multiple of 64 */
+} vat_problem_t;
+
+/* What the planner decided; filled by vat_plan. Shape-only: the same problem
+ * always gives the same plan. */
+typedef struct {
+  int32_t direct;           /* 1: no merge kernel; partial kernel writes out/lse */
+  int32_t group;            /* G = Hq / Hkv */
+  int32_t rows;             /* G * max_qo_len query rows per (request, KV head) */
+  int32_t row_tiles_per_wave; /* 16-row MFMA tiles each wave holds */
+  int32_t waves_rows;       /* waves splitting a row block's rows */
+  int32_t waves_keys;       /* waves splitting each key range */
+  int32_t rows_per_block;   /* M = waves_rows * row_tiles_per_wave * 16 */
+  int32_t row_blocks;       /* RB = ceil(rows / M) */
+  int32_t chunk_keys;       /* prefix chunk length (split mode) */
+  int32_t num_chunk_ids;    /* partial-kernel grid x in split mode */
+  int32_t grid_x, grid_y;   /* partial kernel grid */
+  int32_t threads;          /* partial kernel workgroup size */
+  int32_t lds_bytes;        /* partial kernel dynamic LDS */
+  int32_t merge_grid;       /* merge kernel workgroups (0 when direct) */
+  int32_t merge_threads;
+  int32_t num_cus;          /* compute units planned for */
+  int64_t workspace_bytes;  /* bytes of workspace the call needs (0 when direct) */
+} vat_plan_t;
+
+/* Plan a call: validates the shapes and fills *plan. Host only; touches the
+ * GPU only to read the compute-unit count when problem->num_cus == 0. */
+vat_status_t vat_plan(const vat_problem_t* problem, vat_plan_t* plan);
+
+/* Workspace bytes verify_attention needs for this problem (host only; see
+ * vat_plan for the device query). */
+vat_status_t vat_workspace_size(const vat_problem_t* problem, size_t* bytes);
+
+/* The whole path: partial kernel, then (unless the plan is direct) the
+ * log-sum-exp merge kernel, both on `stream`. sm_scale > 0, k_scale > 0 and
+ * v_scale must be finite. workspace: device memory of at least
+ * vat_workspace_size() bytes, 256-byte aligned (may be NULL when that size
+ * is 0). Host-detectable problems return an error before anything is
+ * enqueued. */
+vat_status_t verify_attention(const vat_problem_t* problem, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* kv_indptr,
+                              const int32_t* kv_indices, const int32_t* last_page_len,
+                              const int32_t* qo_indptr, const uint8_t* mask,
+                              const int32_t* mask_indptr, float sm_scale, float k_scale,
+                              float v_scale, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* The two halves of verify_attention, for timing each kernel on its own
+ * stream position. vat_launch_partial enqueues the partial kernel only (in a
+ * direct plan it writes out and lse); vat_launch_merge enqueues the merge
+ * only (a no-op returning VAT_OK for a direct plan) and must follow a
+ * vat_launch_partial with identical arguments on the same stream. */
+vat_status_t vat_launch_partial(const vat_problem_t* problem, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* kv_indptr,
+                                const int32_t* kv_indices, const int32_t* last_page_len,
+                                const int32_t* qo_indptr, const uint8_t* mask,
+                                const int32_t* mask_indptr, float sm_scale, float k_scale,
+                                float v_scale, void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream);
+vat_status_t vat_launch_merge(const vat_problem_t* problem, const int32_t* kv_indptr,
+                              const int32_t* last_page_len, const int32_t* qo_indptr,
+                              float v_scale, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* vat_status_string(vat_status_t status);
+
+/* ABI version of this header (bumped on any incompatible change). */
+int32_t vat_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_VERIFY_ATTENTION_H */

@@ -1,0 +1,274 @@
+"""Thin ctypes binding of ``libvat.so`` with the C ABI's names.
+
+Argument marshalling only: torch tensors become device pointers, the current
+HIP stream is passed through, status codes become exceptions. All compute
+runs in the library's kernels; if the library is missing this module raises
+instead of falling back to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libvat.so")
+
+VAT_F32, VAT_BF16, VAT_FP8_E4M3FN = 0, 1, 2
+STATUS = {
+    0: "VAT_OK", 1: "VAT_ERR_NULL", 2: "VAT_ERR_SHAPE", 3: "VAT_ERR_UNSUPPORTED",
+    4: "VAT_ERR_ALIGN", 5: "VAT_ERR_WORKSPACE", 6: "VAT_ERR_HIP",
+}
+_VALUE_ERRORS = {1, 2, 3, 4, 5}
+
+
+class VatProblem(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "batch", "num_qo_heads", "num_kv_heads", "head_dim", "page_size", "num_pages",
+        "num_kv_indices", "num_qo_tokens", "max_qo_len", "q_dtype", "kv_dtype", "has_mask",
+        "num_mask_bytes", "num_cus", "chunk_keys")]
+
+
+class VatPlan(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "direct", "group", "rows", "row_tiles_per_wave", "waves_rows", "waves_keys",
+        "rows_per_block", "row_blocks", "chunk_keys", "num_chunk_ids", "grid_x", "grid_y",
+        "threads", "lds_bytes", "merge_grid", "merge_threads", "num_cus")] + [
+        ("workspace_bytes", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class VatError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({_lib_status_string(status)})")
+
+
+class VatValueError(VatError, ValueError):
+    pass
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load the shared library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(p)
+    P = ctypes.POINTER
+    vp = ctypes.c_void_p
+    f = ctypes.c_float
+    lib.vat_plan.argtypes = [P(VatProblem), P(VatPlan)]
+    lib.vat_plan.restype = ctypes.c_int
+    lib.vat_workspace_size.argtypes = [P(VatProblem), P(ctypes.c_size_t)]
+    lib.vat_workspace_size.restype = ctypes.c_int
+    full = [P(VatProblem), vp, vp, vp, vp, vp, vp, vp, vp, vp, f, f, f, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.verify_attention.argtypes = full
+    lib.verify_attention.restype = ctypes.c_int
+    lib.vat_launch_partial.argtypes = full
+    lib.vat_launch_partial.restype = ctypes.c_int
+    lib.vat_launch_merge.argtypes = [P(VatProblem), vp, vp, vp, f, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.vat_launch_merge.restype = ctypes.c_int
+    lib.vat_status_string.argtypes = [ctypes.c_int]
+    lib.vat_status_string.restype = ctypes.c_char_p
+    lib.vat_abi_version.argtypes = []
+    lib.vat_abi_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def _lib_status_string(status: int) -> str:
+    if _lib is None:
+        return ""
+    return _lib.vat_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status == 0:
+        return
+    if status in _VALUE_ERRORS:
+        raise VatValueError(status, where)
+    raise VatError(status, where)
+
+
+# ------------------------------------------------------------------ problem description
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return VAT_F32
+    if t.dtype == torch.bfloat16:
+        return VAT_BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return VAT_FP8_E4M3FN
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def make_problem(*, batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_pages,
+                 num_kv_indices, num_qo_tokens, max_qo_len, q_dtype, kv_dtype, has_mask,
+                 num_mask_bytes=0, num_cus=0, chunk_keys=-1) -> VatProblem:
+    return VatProblem(batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_pages,
+                      num_kv_indices, num_qo_tokens, max_qo_len, q_dtype, kv_dtype,
+                      int(bool(has_mask)), num_mask_bytes, num_cus, chunk_keys)
+
+
+def problem_from_tensors(q, k_cache, kv_indptr, kv_indices, mask=None, max_qo_len=None,
+                         num_cus=0, chunk_keys=-1) -> VatProblem:
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [T, Hq, D] and caches [pages, page_size, Hkv, D]")
+    batch = kv_indptr.numel() - 1
+    T = q.shape[0]
+    if max_qo_len is None:
+        # Shape-only bound: one request may hold every token but the others' one.
+        max_qo_len = T - max(batch - 1, 0) if batch > 0 else 0
+        max_qo_len = max(max_qo_len, 0)
+    return make_problem(
+        batch=batch, num_qo_heads=q.shape[1], num_kv_heads=k_cache.shape[2], head_dim=q.shape[2],
+        page_size=k_cache.shape[1], num_pages=k_cache.shape[0], num_kv_indices=kv_indices.numel(),
+        num_qo_tokens=T, max_qo_len=int(max_qo_len), q_dtype=_dtype_code(q),
+        kv_dtype=_dtype_code(k_cache), has_mask=mask is not None,
+        num_mask_bytes=0 if mask is None else mask.numel(), num_cus=num_cus,
+        chunk_keys=chunk_keys)
+
+
+def vat_plan(problem: VatProblem) -> VatPlan:
+    lib = load()
+    plan = VatPlan()
+    _check(lib.vat_plan(ctypes.byref(problem), ctypes.byref(plan)), "vat_plan")
+    return plan
+
+
+def vat_workspace_size(problem: VatProblem) -> int:
+    lib = load()
+    n = ctypes.c_size_t(0)
+    _check(lib.vat_workspace_size(ctypes.byref(problem), ctypes.byref(n)), "vat_workspace_size")
+    return int(n.value)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream_handle(stream) -> int:
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _check_tensors(q, k_cache, v_cache, idx):
+    for name, t in [("q", q), ("k_cache", k_cache), ("v_cache", v_cache)] + idx:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must have one shape and dtype")
+
+
+def _prepare(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr, mask,
+             mask_indptr, sm_scale, max_qo_len, out, lse, workspace, chunk_keys, num_cus):
+    import torch
+
+    idx = [("kv_indptr", kv_indptr), ("kv_indices", kv_indices), ("last_page_len", last_page_len),
+           ("qo_indptr", qo_indptr), ("mask", mask), ("mask_indptr", mask_indptr)]
+    _check_tensors(q, k_cache, v_cache, idx)
+    for name, t in idx:
+        if t is None:
+            continue
+        want = torch.uint8 if name == "mask" else torch.int32
+        if t.dtype != want:
+            raise ValueError(f"{name} must be {want}")
+    problem = problem_from_tensors(q, k_cache, kv_indptr, kv_indices, mask, max_qo_len,
+                                   num_cus=num_cus, chunk_keys=chunk_keys)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[2])
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    need = vat_workspace_size(problem)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return problem, float(sm_scale), out, lse, workspace, ws_bytes
+
+
+def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr,
+                     mask=None, mask_indptr=None, sm_scale: Optional[float] = None,
+                     k_scale: float = 1.0, v_scale: float = 1.0, max_qo_len: Optional[int] = None,
+                     out=None, lse=None, workspace=None, chunk_keys: int = -1, num_cus: int = 0,
+                     stream=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """Multi-query verification attention over a paged KV cache; returns (out, lse).
+
+    ``sm_scale`` defaults to ``head_dim ** -0.5``; ``max_qo_len`` defaults to
+    the shape-only bound ``T - (B - 1)``; ``chunk_keys`` -1 lets the planner
+    choose the prefix split, 0 forces one work item per request (direct
+    output), a positive multiple of 64 forces that chunk length.
+    """
+    lib = load()
+    problem, sm, out, lse, workspace, ws_bytes = _prepare(
+        q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr, mask, mask_indptr,
+        sm_scale, max_qo_len, out, lse, workspace, chunk_keys, num_cus)
+    st = lib.verify_attention(ctypes.byref(problem), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                              _ptr(kv_indptr), _ptr(kv_indices), _ptr(last_page_len),
+                              _ptr(qo_indptr), _ptr(mask), _ptr(mask_indptr), sm, float(k_scale),
+                              float(v_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                              _stream_handle(stream))
+    _check(st, "verify_attention")
+    return out, lse
+
+
+class PreparedCall:
+    """A call with every pointer fixed, launched without Python-side checks.
+
+    Used for timing: ``partial()`` and ``merge()`` enqueue the two kernels
+    separately, ``__call__`` the whole path.
+    """
+
+    def __init__(self, q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr,
+                 mask=None, mask_indptr=None, sm_scale=None, k_scale=1.0, v_scale=1.0,
+                 max_qo_len=None, out=None, lse=None, workspace=None, chunk_keys=-1, num_cus=0,
+                 stream=None):
+        self.lib = load()
+        (self.problem, self.sm, self.out, self.lse, self.workspace,
+         self.ws_bytes) = _prepare(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
+                                   qo_indptr, mask, mask_indptr, sm_scale, max_qo_len, out, lse,
+                                   workspace, chunk_keys, num_cus)
+        self.keep = (q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr, mask,
+                     mask_indptr)
+        self.k_scale = float(k_scale)
+        self.v_scale = float(v_scale)
+        self.stream = _stream_handle(stream)
+        self.plan = vat_plan(self.problem)
+        self.args = (ctypes.byref(self.problem), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                     _ptr(kv_indptr), _ptr(kv_indices), _ptr(last_page_len), _ptr(qo_indptr),
+                     _ptr(mask), _ptr(mask_indptr), self.sm, self.k_scale, self.v_scale,
+                     _ptr(self.out), _ptr(self.lse), _ptr(self.workspace), self.ws_bytes,
+                     self.stream)
+        self.merge_args = (ctypes.byref(self.problem), _ptr(kv_indptr), _ptr(last_page_len),
+                           _ptr(qo_indptr), self.v_scale, _ptr(self.out), _ptr(self.lse),
+                           _ptr(self.workspace), self.ws_bytes, self.stream)
+
+    def __call__(self):
+        _check(self.lib.verify_attention(*self.args), "verify_attention")
+        return self.out, self.lse
+
+    def partial(self):
+        _check(self.lib.vat_launch_partial(*self.args), "vat_launch_partial")
+
+    def merge(self):
+        _check(self.lib.vat_launch_merge(*self.merge_args), "vat_launch_merge")

@@ -1,0 +1,262 @@
+// C ABI: host validation, shape-only planning and kernel launches on the
+// caller's stream. Never allocates, frees, synchronises or reads device
+// memory, so calls can be captured into a HIP graph.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "plan.h"
+#include "verify_attention.h"
+
+namespace vat {
+const void* partial_kernel(int kv_dtype, int head_dim, int rt);
+const void* merge_kernel(int q_is_f32, int head_dim);
+}  // namespace vat
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];  // 0 = not yet queried
+
+vat_status_t device_cus(int32_t* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return VAT_ERR_HIP;
+  if (dev < kMaxDevices && g_cu_count[dev] > 0) {
+    *cus = g_cu_count[dev];
+    return VAT_OK;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return VAT_ERR_HIP;
+  if (dev < kMaxDevices) g_cu_count[dev] = n;
+  *cus = n;
+  return VAT_OK;
+}
+
+vat_status_t plan_for(const vat_problem_t* p, vat_plan_t* plan) {
+  vat_status_t st = vat::validate_problem(p);
+  if (st != VAT_OK) return st;
+  int32_t cus = p->num_cus;
+  if (cus == 0) {
+    st = device_cus(&cus);
+    if (st != VAT_OK) return st;
+  }
+  return vat::make_plan(p, cus, plan);
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+bool plan_is_empty(const vat_plan_t& plan) { return plan.grid_x == 0 || plan.grid_y == 0; }
+
+int page_shift(int32_t page_size) {
+  int s = 0;
+  while ((1 << s) < page_size) ++s;
+  return s;
+}
+
+// Everything verify_attention checks before enqueueing, shared by the
+// split launch entry points.
+vat_status_t prepare(const vat_problem_t* p, const void* q, const void* k_cache,
+                     const void* v_cache, const int32_t* kv_indptr, const int32_t* kv_indices,
+                     const int32_t* last_page_len, const int32_t* qo_indptr, const uint8_t* mask,
+                     const int32_t* mask_indptr, float sm_scale, float k_scale, float v_scale,
+                     void* out, float* lse, void* workspace, size_t workspace_bytes,
+                     vat_plan_t* plan) {
+  vat_status_t st = plan_for(p, plan);
+  if (st != VAT_OK) return st;
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale) || !(k_scale > 0.f) || !isfinite(k_scale) ||
+      !isfinite(v_scale))
+    return VAT_ERR_SHAPE;
+  if (plan_is_empty(*plan)) return VAT_OK;
+  if (!q || !k_cache || !v_cache || !kv_indptr || !kv_indices || !last_page_len || !qo_indptr ||
+      !out || !lse)
+    return VAT_ERR_NULL;
+  if (p->has_mask && (!mask || !mask_indptr)) return VAT_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(lse, 4) || !aligned(kv_indptr, 4) || !aligned(kv_indices, 4) ||
+      !aligned(last_page_len, 4) || !aligned(qo_indptr, 4) ||
+      (mask_indptr && !aligned(mask_indptr, 4)))
+    return VAT_ERR_ALIGN;
+  if (plan->workspace_bytes > 0) {
+    if (!workspace) return VAT_ERR_NULL;
+    if (workspace_bytes < (size_t)plan->workspace_bytes) return VAT_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return VAT_ERR_ALIGN;
+  }
+  return VAT_OK;
+}
+
+vat_status_t launch_partial(const vat_problem_t* p, const vat_plan_t& plan, const void* q,
+                            const void* k_cache, const void* v_cache, const int32_t* kv_indptr,
+                            const int32_t* kv_indices, const int32_t* last_page_len,
+                            const int32_t* qo_indptr, const uint8_t* mask,
+                            const int32_t* mask_indptr, float sm_scale, float k_scale,
+                            float v_scale, void* out, float* lse, void* workspace,
+                            hipStream_t stream) {
+  vat::PartialArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.last_page_len = last_page_len;
+  a.qo_indptr = qo_indptr;
+  a.mask = p->has_mask ? mask : nullptr;
+  a.mask_indptr = p->has_mask ? mask_indptr : nullptr;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = plan.direct ? nullptr : (float*)workspace;
+  a.part_lse = plan.direct ? nullptr
+                           : (float*)((char*)workspace +
+                                      vat::workspace_lse_offset(plan, p->head_dim, p->num_kv_heads));
+  a.c_log2 = (float)((double)sm_scale * (double)k_scale * 1.4426950408889634);
+  a.v_scale = v_scale;
+  a.batch = p->batch;
+  a.hq = p->num_qo_heads;
+  a.hkv = p->num_kv_heads;
+  a.group = plan.group;
+  a.tokens = p->num_qo_tokens;
+  a.page_shift = page_shift(p->page_size);
+  a.num_pages = p->num_pages;
+  a.num_kv_indices = p->num_kv_indices;
+  a.num_mask_bytes = p->has_mask ? p->num_mask_bytes : 0;
+  a.rows_per_block = plan.rows_per_block;
+  a.row_blocks = plan.row_blocks;
+  a.waves_rows = plan.waves_rows;
+  a.waves_keys = plan.waves_keys;
+  a.direct = plan.direct;
+  a.chunk_keys = plan.direct ? 1 : plan.chunk_keys;
+  a.num_ids = plan.num_chunk_ids;
+  a.has_mask = p->has_mask;
+  const void* fn = vat::partial_kernel(p->kv_dtype, p->head_dim, plan.row_tiles_per_wave);
+  if (plan.lds_bytes > 65536) {
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, plan.lds_bytes) !=
+        hipSuccess)
+      return VAT_ERR_HIP;
+  }
+  void* args[] = {&a};
+  hipError_t e = hipLaunchKernel(fn, dim3(plan.grid_x, plan.grid_y, 1), dim3(plan.threads, 1, 1),
+                                 args, (size_t)plan.lds_bytes, stream);
+  return e == hipSuccess ? VAT_OK : VAT_ERR_HIP;
+}
+
+vat_status_t launch_merge(const vat_problem_t* p, const vat_plan_t& plan,
+                          const int32_t* kv_indptr, const int32_t* last_page_len,
+                          const int32_t* qo_indptr, float v_scale, void* out, float* lse,
+                          void* workspace, hipStream_t stream) {
+  if (plan.direct || plan.merge_grid == 0) return VAT_OK;
+  vat::MergeArgs a;
+  a.part_o = (const float*)workspace;
+  a.part_lse =
+      (const float*)((char*)workspace + vat::workspace_lse_offset(plan, p->head_dim, p->num_kv_heads));
+  a.kv_indptr = kv_indptr;
+  a.last_page_len = last_page_len;
+  a.qo_indptr = qo_indptr;
+  a.out = out;
+  a.lse = lse;
+  a.v_scale = v_scale;
+  a.batch = p->batch;
+  a.hq = p->num_qo_heads;
+  a.hkv = p->num_kv_heads;
+  a.group = plan.group;
+  a.tokens = p->num_qo_tokens;
+  a.page_shift = page_shift(p->page_size);
+  a.num_kv_indices = p->num_kv_indices;
+  a.rows_per_block = plan.rows_per_block;
+  a.row_blocks = plan.row_blocks;
+  a.chunk_keys = plan.chunk_keys;
+  a.num_ids = plan.num_chunk_ids;
+  a.row_groups = (plan.rows_per_block + vat::kMergeRows - 1) / vat::kMergeRows;
+  const void* fn = vat::merge_kernel(p->q_dtype == VAT_F32, p->head_dim);
+  void* args[] = {&a};
+  hipError_t e = hipLaunchKernel(fn, dim3(plan.merge_grid, 1, 1), dim3(plan.merge_threads, 1, 1),
+                                 args, 0, stream);
+  return e == hipSuccess ? VAT_OK : VAT_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+vat_status_t vat_plan(const vat_problem_t* problem, vat_plan_t* plan) {
+  if (!problem || !plan) return VAT_ERR_NULL;
+  return plan_for(problem, plan);
+}
+
+vat_status_t vat_workspace_size(const vat_problem_t* problem, size_t* bytes) {
+  if (!problem || !bytes) return VAT_ERR_NULL;
+  vat_plan_t plan;
+  vat_status_t st = plan_for(problem, &plan);
+  if (st != VAT_OK) return st;
+  *bytes = (size_t)plan.workspace_bytes;
+  return VAT_OK;
+}
+
+vat_status_t vat_launch_partial(const vat_problem_t* problem, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* kv_indptr,
+                                const int32_t* kv_indices, const int32_t* last_page_len,
+                                const int32_t* qo_indptr, const uint8_t* mask,
+                                const int32_t* mask_indptr, float sm_scale, float k_scale,
+                                float v_scale, void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  vat_plan_t plan;
+  vat_status_t st = prepare(problem, q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
+                            qo_indptr, mask, mask_indptr, sm_scale, k_scale, v_scale, out, lse,
+                            workspace, workspace_bytes, &plan);
+  if (st != VAT_OK || plan_is_empty(plan)) return st;
+  return launch_partial(problem, plan, q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
+                        qo_indptr, mask, mask_indptr, sm_scale, k_scale, v_scale, out, lse,
+                        workspace, (hipStream_t)stream);
+}
+
+vat_status_t vat_launch_merge(const vat_problem_t* problem, const int32_t* kv_indptr,
+                              const int32_t* last_page_len, const int32_t* qo_indptr,
+                              float v_scale, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  vat_plan_t plan;
+  vat_status_t st = plan_for(problem, &plan);
+  if (st != VAT_OK) return st;
+  if (!isfinite(v_scale)) return VAT_ERR_SHAPE;
+  if (plan_is_empty(plan) || plan.direct) return VAT_OK;
+  if (!kv_indptr || !last_page_len || !qo_indptr || !out || !lse || !workspace) return VAT_ERR_NULL;
+  if (workspace_bytes < (size_t)plan.workspace_bytes) return VAT_ERR_WORKSPACE;
+  if (!aligned(workspace, 256) || !aligned(out, 16) || !aligned(lse, 4)) return VAT_ERR_ALIGN;
+  return launch_merge(problem, plan, kv_indptr, last_page_len, qo_indptr, v_scale, out, lse,
+                      workspace, (hipStream_t)stream);
+}
+
+vat_status_t verify_attention(const vat_problem_t* problem, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* kv_indptr,
+                              const int32_t* kv_indices, const int32_t* last_page_len,
+                              const int32_t* qo_indptr, const uint8_t* mask,
+                              const int32_t* mask_indptr, float sm_scale, float k_scale,
+                              float v_scale, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  vat_plan_t plan;
+  vat_status_t st = prepare(problem, q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
+                            qo_indptr, mask, mask_indptr, sm_scale, k_scale, v_scale, out, lse,
+                            workspace, workspace_bytes, &plan);
+  if (st != VAT_OK || plan_is_empty(plan)) return st;
+  st = launch_partial(problem, plan, q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
+                      qo_indptr, mask, mask_indptr, sm_scale, k_scale, v_scale, out, lse,
+                      workspace, (hipStream_t)stream);
+  if (st != VAT_OK) return st;
+  return launch_merge(problem, plan, kv_indptr, last_page_len, qo_indptr, v_scale, out, lse,
+                      workspace, (hipStream_t)stream);
+}
+
+const char* vat_status_string(vat_status_t status) {
+  switch (status) {
+    case VAT_OK: return "ok";
+    case VAT_ERR_NULL: return "a required pointer is NULL";
+    case VAT_ERR_SHAPE: return "inconsistent shapes or invalid scales";
+    case VAT_ERR_UNSUPPORTED: return "head_dim, page_size, dtype pair or mask length not supported";
+    case VAT_ERR_ALIGN: return "q, caches, out or workspace misaligned";
+    case VAT_ERR_WORKSPACE: return "workspace too small";
+    case VAT_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t vat_abi_version(void) { return 1; }
+
+}  // extern "C"

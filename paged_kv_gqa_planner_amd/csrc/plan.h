@@ -1,0 +1,74 @@
+// Host planner and kernel argument blocks. Plain C++: no HIP headers, so the
+// planner builds and runs on a machine without a GPU.
+#pragma once
+
+#include <stdint.h>
+
+#include "verify_attention.h"
+
+namespace vat {
+
+// Keys each wave consumes per step of its key loop (two 16-key MFMA tiles).
+constexpr int kStepKeys = 32;
+// Threads per partial-kernel workgroup: four wave64s.
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+// Query rows merged per merge-kernel workgroup.
+constexpr int kMergeRows = 4;
+constexpr int kMergeThreads = 256;
+// Smallest prefix chunk the planner picks, in keys.
+constexpr int kMinChunkKeys = 256;
+// Prefix chunks are multiples of this many keys.
+constexpr int kChunkQuantum = 64;
+// Largest draft count per request a bit-packed mask may carry (one 64-bit
+// register holds a row).
+constexpr int kMaxMaskedLen = 64;
+
+// Arguments of the partial kernel; every field is a plain pointer or integer.
+struct PartialArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* last_page_len;
+  const int32_t* qo_indptr;
+  const uint8_t* mask;
+  const int32_t* mask_indptr;
+  void* out;
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  float c_log2;   // sm_scale * k_scale * log2(e): raw logit -> base-2 exponent
+  float v_scale;
+  int32_t batch, hq, hkv, group, tokens;
+  int32_t page_shift, num_pages, num_kv_indices, num_mask_bytes;
+  int32_t rows_per_block, row_blocks, waves_rows, waves_keys;
+  int32_t direct, chunk_keys, num_ids, has_mask;
+};
+
+// Arguments of the merge kernel.
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* kv_indptr;
+  const int32_t* last_page_len;
+  const int32_t* qo_indptr;
+  void* out;
+  float* lse;
+  float v_scale;
+  int32_t batch, hq, hkv, group, tokens;
+  int32_t page_shift, num_kv_indices;
+  int32_t rows_per_block, row_blocks, chunk_keys, num_ids, row_groups;
+};
+
+// Shape validation (host-detectable errors only).
+vat_status_t validate_problem(const vat_problem_t* p);
+
+// Shape-only plan for `num_cus` compute units. Calls validate_problem.
+vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan);
+
+// Byte offset of the partial-lse array inside the workspace.
+int64_t workspace_lse_offset(const vat_plan_t& plan, int32_t head_dim, int32_t num_kv_heads);
+
+}  // namespace vat

@@ -1,0 +1,229 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Tolerances: out within 1e-5 (fp32 inputs) or 2e-2 (bf16 / fp8 inputs, bf16
+output) absolute, lse within 1e-3, -inf exactly where the oracle has -inf,
+no NaN. Page-index and mask handling must be bit-exact: results are bitwise
+equal under a page-pool permutation, for a chain mask versus causal, and
+from run to run.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_helpers import compare, oracle_of, rows_of, run_gpu, say, to_device, to_f64
+from workloads import make_case, make_config
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------- the five workloads
+
+
+CONFIG_CASES = [(1, None), (2, None), (3, 4096), (3, 16384), (3, 32768), (4, None), (5, None)]
+
+
+@pytest.mark.parametrize("cid,prefix", CONFIG_CASES, ids=lambda x: str(x))
+def test_config_parity(gpu_lib, cid, prefix):
+    p = make_config(cid, prefix=prefix or 4096)
+    say(f"[config {cid} prefix={prefix}] {p.name}")
+    plan = gpu_lib.vat_plan(_problem(gpu_lib, p)).as_dict()
+    say(f"  plan {plan}")
+    out, lse = run_gpu(gpu_lib, p)
+    got_o, got_l = to_f64(out, lse)
+    requests = None if cid != 4 else [0, 9]
+    ref_o, ref_l = oracle_of(p, requests=requests)
+    rows = None if requests is None else rows_of(p, requests)
+    eo, el = compare(p, got_o, got_l, ref_o, ref_l, rows=rows, what=f"config {cid}")
+    say(f"  max|out err| {eo:.3e}  max|lse err| {el:.3e}")
+
+
+def _problem(lib, p, **kw):
+    t = to_device(p)
+    return lib.problem_from_tensors(t["q"], t["k_cache"], t["kv_indptr"], t["kv_indices"],
+                                    t["mask"], p.max_qo_len, **kw)
+
+
+# ---------------------------------------------------------------- seeded small-shape fuzz
+
+
+def _fuzz_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    pairs = [("f32", "f32"), ("bf16", "bf16"), ("bf16", "e4m3")]
+    q_dt, kv_dt = pairs[seed % 3]
+    D = [64, 128][(seed // 3) % 2]
+    B = int(rng.integers(1, 5))
+    Hkv = int(rng.integers(1, 3))
+    G = int(rng.choice([1, 3, 4, 8]))
+    ps = int(rng.choice([1, 4, 16, 64]))
+    mask_kind = ["causal", "tree", "random", "chain"][seed % 4]
+    Lmax = 20 if mask_kind != "causal" else 40
+    lens = [int(x) for x in rng.integers(1, Lmax + 1, size=B)]
+    prefixes = [int(x) for x in rng.integers(0, 301, size=B)]
+    chunk = int(rng.choice([-1, 0, 64, 128]))
+    p = make_case(seed, prefix_lens=prefixes, qo_lens=lens, num_qo_heads=G * Hkv,
+                  num_kv_heads=Hkv, head_dim=D, page_size=ps, q_dtype=q_dt, kv_dtype=kv_dt,
+                  mask_kind=mask_kind, fp8_absmax_scales=(kv_dt == "e4m3"), mask_density=0.4,
+                  mask_pad_bytes=int(seed % 3), extra_indices=int(seed % 5))
+    return p, chunk
+
+
+@pytest.mark.parametrize("seed", list(range(36)))
+def test_fuzz_small_shapes(gpu_lib, seed):
+    p, chunk = _fuzz_case(seed)
+    say(f"[fuzz {seed}] B={p.batch} Hq={p.num_qo_heads} Hkv={p.num_kv_heads} D={p.head_dim} "
+        f"ps={p.page_size} {p.q_dtype}/{p.kv_dtype} mask={p.info['mask_kind']} "
+        f"L={p.info['qo_lens']} prefix={p.info['prefix_lens']} chunk={chunk}")
+    out, lse = run_gpu(gpu_lib, p, chunk_keys=chunk)
+    compare(p, *to_f64(out, lse), *oracle_of(p), what=f"fuzz {seed}")
+
+
+# ---------------------------------------------------------------- edge cases
+
+
+EDGE = {
+    "prefix0_L1": dict(prefix_lens=[0], qo_lens=[1]),
+    "kv_len_multiple_of_page": dict(prefix_lens=[27, 11], qo_lens=[5, 5]),
+    "last_page_len_1": dict(prefix_lens=[16, 32], qo_lens=[1, 1]),
+    "verify_straddles_page": dict(prefix_lens=[14, 30], qo_lens=[7, 9]),
+    "empty_request_between": dict(prefix_lens=[40, 9, 70], qo_lens=[3, 0, 4]),
+    "decode_many_requests": dict(prefix_lens=list(range(0, 640, 10)), qo_lens=[1] * 64),
+    "long_prefill_causal": dict(prefix_lens=[0, 35], qo_lens=[300, 129]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+@pytest.mark.parametrize("chunk", [-1, 0, 64])
+def test_edge_cases(gpu_lib, name, chunk):
+    kw = EDGE[name]
+    p = make_case(77, num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=16, **kw)
+    say(f"[edge {name} chunk={chunk}]")
+    out, lse = run_gpu(gpu_lib, p, chunk_keys=chunk)
+    compare(p, *to_f64(out, lse), *oracle_of(p), what=name)
+
+
+def test_fully_masked_rows_give_zero_and_minus_inf(gpu_lib):
+    p = make_case(5, prefix_lens=[0, 0], qo_lens=[6, 9], num_qo_heads=4, num_kv_heads=1,
+                  head_dim=64, page_size=4, q_dtype="f32", kv_dtype="f32", mask_kind="random",
+                  mask_density=0.2)
+    ref_o, ref_l = oracle_of(p)
+    assert np.isneginf(ref_l).any(), "seed should produce a fully masked row"
+    for chunk in (-1, 0, 64):
+        say(f"[fully masked chunk={chunk}]")
+        out, lse = run_gpu(gpu_lib, p, chunk_keys=chunk)
+        got_o, got_l = to_f64(out, lse)
+        compare(p, got_o, got_l, ref_o, ref_l, what="fully masked")
+        assert np.all(got_o[np.isneginf(ref_l)] == 0.0)
+
+
+def test_empty_batch_and_no_tokens(gpu_lib):
+    import torch
+
+    dev = "cuda"
+    q = torch.zeros(0, 4, 64, dtype=torch.bfloat16, device=dev)
+    kc = torch.zeros(2, 16, 1, 64, dtype=torch.bfloat16, device=dev)
+    for B in (0, 2):
+        kv_indptr = torch.zeros(B + 1, dtype=torch.int32, device=dev)
+        idx = torch.zeros(1, dtype=torch.int32, device=dev)
+        lpl = torch.ones(B, dtype=torch.int32, device=dev)
+        qo = torch.zeros(B + 1, dtype=torch.int32, device=dev)
+        out, lse = gpu_lib.verify_attention(q, kc, kc.clone(), kv_indptr, idx, lpl, qo)
+        torch.cuda.synchronize()
+        assert out.shape == (0, 4, 64) and lse.shape == (0, 4)
+
+
+# ---------------------------------------------------------------- bit-exactness
+
+
+def test_page_permutation_is_bitwise_invariant(gpu_lib):
+    base = make_case(31, prefix_lens=[500, 77, 1200], qo_lens=[5, 3, 8], num_qo_heads=16,
+                     num_kv_heads=4, head_dim=128, mask_kind="tree")
+    t = to_device(base)
+    out0, lse0 = run_gpu(gpu_lib, base, tensors=t)
+    # Move every page to a new physical slot and remap the table.
+    rng = np.random.default_rng(3)
+    perm = rng.permutation(base.num_pages)
+    k2 = np.empty_like(base.k_cache)
+    v2 = np.empty_like(base.v_cache)
+    k2[perm] = base.k_cache
+    v2[perm] = base.v_cache
+    idx2 = perm[base.kv_indices].astype(np.int32)
+    moved = make_case(31, prefix_lens=[500, 77, 1200], qo_lens=[5, 3, 8], num_qo_heads=16,
+                      num_kv_heads=4, head_dim=128, mask_kind="tree")
+    moved.k_cache, moved.v_cache, moved.kv_indices = k2, v2, idx2
+    out1, lse1 = run_gpu(gpu_lib, moved)
+    assert torch.equal(out0.view(torch.int16), out1.view(torch.int16))
+    assert torch.equal(lse0, lse1)
+
+
+@pytest.mark.parametrize("chunk", [-1, 0])
+def test_chain_mask_bitwise_equals_causal(gpu_lib, chunk):
+    kw = dict(prefix_lens=[100, 3, 640], qo_lens=[6, 4, 17], num_qo_heads=8, num_kv_heads=2,
+              head_dim=128)
+    pc = make_case(41, mask_kind="causal", **kw)
+    pm = make_case(41, mask_kind="chain", **kw)
+    assert np.array_equal(pc.k_cache.view(np.uint16), pm.k_cache.view(np.uint16))
+    oc, lc = run_gpu(gpu_lib, pc, chunk_keys=chunk)
+    om, lm = run_gpu(gpu_lib, pm, chunk_keys=chunk)
+    assert torch.equal(oc.view(torch.int16), om.view(torch.int16))
+    assert torch.equal(lc, lm)
+
+
+def test_repeat_runs_are_bitwise_identical(gpu_lib):
+    p = make_config(2)
+    t = to_device(p)
+    o1, l1 = run_gpu(gpu_lib, p, tensors=t)
+    o1, l1 = o1.clone(), l1.clone()
+    for _ in range(3):
+        o2, l2 = run_gpu(gpu_lib, p, tensors=t)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("chunk", [0, 64, 128, 256, 512, 2048])
+def test_any_split_matches_oracle(gpu_lib, chunk):
+    p = make_config(3, prefix=4096)
+    say(f"[split chunk={chunk}]")
+    out, lse = run_gpu(gpu_lib, p, chunk_keys=chunk)
+    compare(p, *to_f64(out, lse), *oracle_of(p), what=f"chunk {chunk}")
+
+
+# ---------------------------------------------------------------- graph capture
+
+
+def test_hip_graph_capture_and_replay(gpu_lib):
+    p = make_config(2)
+    t = to_device(p)
+    # Warm up (loads the library, plans, allocates the workspace) outside capture.
+    ws_size = gpu_lib.vat_workspace_size(_problem(gpu_lib, p))
+    ws = torch.empty(ws_size, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(t["q"])
+    lse = torch.empty(t["q"].shape[0], t["q"].shape[1], dtype=torch.float32, device="cuda")
+    call = dict(mask=t["mask"], mask_indptr=t["mask_indptr"], sm_scale=p.sm_scale,
+                k_scale=p.k_scale, v_scale=p.v_scale, max_qo_len=p.max_qo_len, out=out, lse=lse,
+                workspace=ws)
+    args = (t["q"], t["k_cache"], t["v_cache"], t["kv_indptr"], t["kv_indices"],
+            t["last_page_len"], t["qo_indptr"])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        gpu_lib.verify_attention(*args, **call)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gpu_lib.verify_attention(*args, **call)
+    # New inputs in the same buffers, then replay several times with eager work between.
+    p2 = make_config(2, seed=99)
+    t2 = to_device(p2)
+    for name in ("q", "k_cache", "v_cache", "kv_indices"):
+        t[name].copy_(t2[name])
+    ref_o, ref_l = oracle_of(p2)
+    for rep in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        compare(p2, *to_f64(out, lse), ref_o, ref_l, what=f"graph replay {rep}")
+        eager_o, eager_l = gpu_lib.verify_attention(*args, **{**call, "out": None, "lse": None,
+                                                               "workspace": None})
+        torch.cuda.synchronize()
+        assert torch.equal(eager_o.view(torch.int16), out.view(torch.int16))

@@ -47,7 +47,7 @@ CONFIG_NAMES = {
     2: "GQA chain verify bf16 (B8 Hq32 Hkv8 D128, prefix 2048, L5 causal)",
     3: "tree verify bf16 at batch 1 (Hq32 Hkv8 D128, L17 tree, prefix {p})",
     4: "GQA causal prefill bf16 (B10x1024, Hq64 Hkv8 D128)",
-    5: "mixed-dtype dynamic-draft verify (B64 Hq32 Hkv8 D128, bf16 Q, e4m3 KV, prefix U[512,8192], L U{1..8})",
+    5: "mixed-dtype dynamic-draft verify (B64 Hq32 Hkv8 D128, bf16 Q, e4m3 KV, prefix U[512,8192], L U{{1..8}})",
 }
 
 
