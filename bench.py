@@ -1,0 +1,310 @@
+"""Throughput of multi-query verification attention over a paged KV cache on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--prefix 4096]
+
+One step is one ``verify_attention`` call -- partial kernel plus log-sum-exp
+merge -- over one batch of seeded synthetic inputs already resident in HBM.
+Successive steps read different batches: ``--copies`` physically permuted
+copies of the page pool (each with its own page table), together larger than
+the 256 MB Infinity Cache, so every step streams its KV cache from HBM.
+
+Before timing, the output of every copy is checked: copy 0 against the CPU
+oracle at the parity tolerances, the others bitwise against copy 0. The
+timed K steps run back to back on one stream; the stream is first held by a
+short GPU sleep so that the host has queued all K steps before the first
+one starts and HIP events measure GPU time only. Events around each partial
+kernel give its average duration, from which the roofline fraction is
+computed with the algorithmic bytes (KV-bound workloads) or FLOPs (prefill).
+
+Prints one JSON line. The oracle (single-threaded NumPy float64) is timed on
+the host on the same workload as the ``cpu_baseline`` leg.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+METRIC = "verified query-tokens/s + achieved KV-read HBM GB/s (% of peak), 1 MI355X"
+WORKLOAD_NAMES = {
+    1: "tiny MQA verify fp32: B2 Hq4 Hkv1 D64, prefix 37/100, L4 causal, page 16 (32-page pool)",
+    2: "GQA chain verify bf16: B8 Hq32 Hkv8 D128, prefix 2048, L5 causal, page 16",
+    3: "tree verify bf16 at batch 1: Hq32 Hkv8 D128, L17 random tree, prefix {p}, page 16",
+    4: "GQA causal prefill bf16: B10 x 1024 packed, Hq64 Hkv8 D128, page 16",
+    5: "bf16 Q + fp8 e4m3 KV dynamic-draft verify: B64 Hq32 Hkv8 D128, prefix U[512,8192], L U{{1..8}}, page 16",
+}
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("device_common.h", "stream_kernel.hip", "tile_kernel.hip", "merge_kernel.hip",
+                 "plan.cpp", "plan.h", "api.hip"):
+        with open(os.path.join(ROOT, "paged_kv_gqa_planner_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_work(p):
+    """KV bytes (every cached entry of every request, K and V, once per KV
+    head) and the FLOPs of QK^T and PV over the visible (query, key) pairs."""
+    from workloads import kv_bytes
+
+    kvb = kv_bytes(p)
+    pairs = 0
+    for b in range(p.batch):
+        L = int(p.qo_indptr[b + 1] - p.qo_indptr[b])
+        pages = int(p.kv_indptr[b + 1] - p.kv_indptr[b])
+        kv_len = 0 if pages == 0 else (pages - 1) * p.page_size + int(p.last_page_len[b])
+        prefix = kv_len - L
+        if p.mask is None:
+            pairs += L * prefix + L * (L + 1) // 2
+        else:
+            seg = p.mask[int(p.mask_indptr[b]):]
+            bits = sum(int((seg[i // 8] >> (i % 8)) & 1) for i in range(L * L))
+            pairs += L * prefix + bits
+    flops = 4 * p.head_dim * p.num_qo_heads * pairs
+    return kvb, flops
+
+
+def timed_oracle(p, min_seconds: float, requests=None):
+    """Oracle wall time on this host with one BLAS thread; repeats the sample
+    until ``min_seconds`` have passed (at least once)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import verify_attention as oracle_va
+
+    reps = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        while True:
+            ref = oracle_va(p.q, p.k_cache, p.v_cache, p.kv_indptr, p.kv_indices, p.last_page_len,
+                            p.qo_indptr, p.mask, p.mask_indptr, sm_scale=p.sm_scale,
+                            k_scale=p.k_scale, v_scale=p.v_scale, q_dtype=p.q_dtype,
+                            kv_dtype=p.kv_dtype, requests=requests)
+            reps += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+    return ref, (time.perf_counter() - t0), reps
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--prefix", type=int, default=4096, help="prefix length for config 3")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="page-pool copies rotated over the steps (0: enough for >= 1 GiB)")
+    ap.add_argument("--chunk-keys", type=int, default=-1, help="planner override (-1: planner)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum host time spent timing the oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from paged_kv_gqa_planner_amd import binding
+    from tests.gpu_helpers import TOL_LSE, TOL_OUT, to_device
+    from workloads import make_config
+
+    binding.load()  # fails loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    p = make_config(args.config, prefix=args.prefix)
+    kvb, flops = algorithmic_work(p)
+    tokens = p.num_tokens
+    base = to_device(p, dev)
+    pool_bytes = 2 * base["k_cache"].numel() * base["k_cache"].element_size()
+    copies = args.copies or max(2, math.ceil((1 << 30) / pool_bytes))
+
+    # Physically permuted copies of the page pool, each with its own table.
+    gen = torch.Generator(device="cpu").manual_seed(1234)
+    batches = []
+    for i in range(copies):
+        if i == 0:
+            kc, vc, idx = base["k_cache"], base["v_cache"], base["kv_indices"]
+        else:
+            perm = torch.randperm(p.num_pages, generator=gen).to(dev)
+            kc = torch.empty_like(base["k_cache"])
+            vc = torch.empty_like(base["v_cache"])
+            kc[perm] = base["k_cache"]
+            vc[perm] = base["v_cache"]
+            idx = base["kv_indices"].clone()
+            used = int(p.kv_indptr[-1])
+            idx[:used] = perm[base["kv_indices"][:used].long()].to(torch.int32)
+        call = binding.PreparedCall(
+            base["q"], kc, vc, base["kv_indptr"], idx, base["last_page_len"], base["qo_indptr"],
+            base["mask"], base["mask_indptr"], sm_scale=p.sm_scale, k_scale=p.k_scale,
+            v_scale=p.v_scale, max_qo_len=p.max_qo_len, chunk_keys=args.chunk_keys)
+        batches.append(call)
+    torch.cuda.synchronize()
+
+    # ---- verification: copy 0 against the oracle, the others bitwise against copy 0
+    sample_requests = None if args.config != 4 else [0, p.batch - 1]
+    cpu = None
+    if not args.no_cpu_baseline:
+        ref, cpu_s, cpu_reps = timed_oracle(p, args.cpu_seconds, sample_requests)
+        cpu = (cpu_s, cpu_reps)
+    else:
+        from tests.gpu_helpers import oracle_of
+        ref = oracle_of(p, requests=sample_requests)
+    o0, l0 = batches[0]()
+    torch.cuda.synchronize()
+    o0 = o0.clone()
+    l0 = l0.clone()
+    got_o = o0.float().cpu().double().numpy()
+    got_l = l0.cpu().double().numpy()
+    rows = np.arange(tokens)
+    if sample_requests is not None:
+        rows = np.concatenate([np.arange(p.qo_indptr[b], p.qo_indptr[b + 1]) for b in sample_requests])
+    ref_o, ref_l = ref[0][rows], ref[1][rows]
+    go, gl = got_o[rows], got_l[rows]
+    ninf_ok = bool(np.array_equal(np.isneginf(ref_l), np.isneginf(gl)))
+    fin = ~np.isneginf(ref_l)
+    err_o = float(np.abs(go - ref_o).max())
+    err_l = float(np.abs(gl[fin] - ref_l[fin]).max()) if fin.any() else 0.0
+    verified = (ninf_ok and not np.isnan(go).any() and err_o <= TOL_OUT[p.q_dtype]
+                and err_l <= TOL_LSE)
+    for call in batches[1:]:
+        o, l = call()
+        torch.cuda.synchronize()
+        verified = verified and torch.equal(o.view(torch.int16), o0.view(torch.int16)) \
+            and torch.equal(l, l0)
+
+    # ---- warmup
+    for i in range(args.warmup):
+        batches[i % copies]()
+    torch.cuda.synchronize()
+
+    # ---- timed region
+    K = args.steps
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    # Calibrate the GPU sleep that holds the stream while the host queues K steps.
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    torch.cuda._sleep(1_000_000)
+    c1.record()
+    torch.cuda.synchronize()
+    cycles_per_ms = 1_000_000 / max(c0.elapsed_time(c1), 1e-3)
+    t_host = time.perf_counter()
+    for i in range(3):
+        batches[i % copies].partial()
+        batches[i % copies].merge()
+    host_per_step = (time.perf_counter() - t_host) / 3
+    torch.cuda.synchronize()
+    hold_ms = 20.0 + 2.0 * K * host_per_step * 1e3
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(hold_ms * cycles_per_ms))
+    start.record()
+    t_enq = time.perf_counter()
+    for i in range(K):
+        call = batches[i % copies]
+        ev_a[i].record()
+        call.partial()
+        ev_b[i].record()
+        call.merge()
+    end.record()
+    enqueue_ms = (time.perf_counter() - t_enq) * 1e3
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    partial_ms = [ev_a[i].elapsed_time(ev_b[i]) for i in range(K)]
+    gpu_ran_ahead = enqueue_ms < hold_ms
+
+    ms_per_step = total_ms / K
+    value = tokens * K / (total_ms * 1e-3)
+    part_avg = float(np.mean(partial_ms))
+    part_med = float(np.median(partial_ms))
+    plan = batches[0].plan.as_dict()
+    if args.config == 4:
+        achieved = flops / (part_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    else:
+        achieved = kvb / (part_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4)}
+    roof["traffic"] = None
+    src_hash = kernel_source_hash()
+    if os.path.exists(PROFILE_TRAFFIC):
+        with open(PROFILE_TRAFFIC) as f:
+            tr = json.load(f)
+        entry = tr.get(str(args.config) if args.config != 3 else f"3@{args.prefix}")
+        if entry and entry.get("source_hash") == src_hash:
+            roof["traffic"] = entry.get("bytes_per_launch")
+    roof["kernel"] = "vat_partial"
+    roof["algorithmic_bytes_per_launch"] = kvb
+    roof["algorithmic_flops_per_launch"] = flops
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16"}[p.q_dtype] + ("+e4m3kv" if p.kv_dtype == "e4m3" else ""),
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.config].format(p=args.prefix),
+                   "batch": p.batch, "query_tokens": tokens, "kv_bytes": kvb,
+                   "parallelism": "single GPU", "page_pool_copies": copies},
+        "kv_read_gbps_step": round(kvb / (ms_per_step * 1e-3) / 1e9, 1),
+        "kv_frac_of_peak_step": round(kvb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": roof,
+        "partial_kernel_ms": {"mean": round(part_avg, 5), "median": round(part_med, 5),
+                              "min": round(float(np.min(partial_ms)), 5)},
+        "verified": bool(verified),
+        "parity": {"max_out_err": err_o, "max_lse_err": err_l,
+                   "tol_out": TOL_OUT[p.q_dtype], "tol_lse": TOL_LSE,
+                   "sample": "all requests" if sample_requests is None else
+                   f"requests {sample_requests}"},
+        "plan": plan,
+        "gpu_ran_ahead_of_host": bool(gpu_ran_ahead),
+        "kernel_source": src_hash,
+    }
+    if cpu is not None:
+        cpu_s, reps = cpu
+        cpu_tokens = tokens if sample_requests is None else int(
+            sum(p.qo_indptr[b + 1] - p.qo_indptr[b] for b in sample_requests))
+        line["cpu_baseline"] = {
+            "value": round(cpu_tokens * reps / cpu_s, 3), "unit": "query-tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": ("whole workload" if sample_requests is None else
+                       f"requests {sample_requests} of the workload") +
+                      f", repeated {reps}x, {cpu_s:.1f} s, NumPy float64 with one BLAS thread"}
+    print(json.dumps(line), flush=True)
+    if not verified:
+        sys.exit(3)
+
+
+if __name__ == "__main__":
+    main()

@@ -100,15 +100,19 @@ typedef struct {
   int32_t has_mask;       /* 0: causal drafts (mask ignored); 1: bit-packed mask */
   int32_t num_mask_bytes; /* size of mask when has_mask */
   int32_t num_cus;        /* compute units to plan for; 0 = query the current device */
-  int32_t chunk_keys;     /* -1: planner; 0: no prefix split (one work item per
-                             request, KV head and row block writes out directly);
-                             > 0: prefix chunk length in keys, multiple of 64 */
+  int32_t chunk_keys;     /* -1: planner; 0: no split (one work item per request,
+                             KV head and row block writes out directly);
+                             > 0: chunk length in keys, multiple of 16 */
 } vat_problem_t;
 
 /* What the planner decided; filled by vat_plan. Shape-only: the same problem
  * always gives the same plan. */
 typedef struct {
-  int32_t direct;           /* 1: no merge kernel; partial kernel writes out/lse */
+  int32_t direct;           /* 1: every request fits one chunk: no merge kernel,
+                               the partial kernel writes out/lse itself */
+  int32_t kernel;           /* 1: LDS-ring streaming kernel (bf16/fp8 KV, <= 80
+                               query rows per KV head); 0: row-tiled kernel */
+  int32_t stages;           /* streaming kernel: 64-key stages in flight in LDS */
   int32_t group;            /* G = Hq / Hkv */
   int32_t rows;             /* G * max_qo_len query rows per (request, KV head) */
   int32_t row_tiles_per_wave; /* 16-row MFMA tiles each wave holds */
@@ -116,8 +120,9 @@ typedef struct {
   int32_t waves_keys;       /* waves splitting each key range */
   int32_t rows_per_block;   /* M = waves_rows * row_tiles_per_wave * 16 */
   int32_t row_blocks;       /* RB = ceil(rows / M) */
-  int32_t chunk_keys;       /* prefix chunk length (split mode) */
-  int32_t num_chunk_ids;    /* partial-kernel grid x in split mode */
+  int32_t chunk_keys;       /* keys per chunk: request b's keys [0, kv_len_b) form
+                               ceil(kv_len_b / chunk_keys) work items */
+  int32_t num_chunk_ids;    /* partial-kernel grid x */
   int32_t grid_x, grid_y;   /* partial kernel grid */
   int32_t threads;          /* partial kernel workgroup size */
   int32_t lds_bytes;        /* partial kernel dynamic LDS */

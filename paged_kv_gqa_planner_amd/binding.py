@@ -33,7 +33,7 @@ class VatProblem(ctypes.Structure):
 
 class VatPlan(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
-        "direct", "group", "rows", "row_tiles_per_wave", "waves_rows", "waves_keys",
+        "direct", "kernel", "stages", "group", "rows", "row_tiles_per_wave", "waves_rows", "waves_keys",
         "rows_per_block", "row_blocks", "chunk_keys", "num_chunk_ids", "grid_x", "grid_y",
         "threads", "lds_bytes", "merge_grid", "merge_threads", "num_cus")] + [
         ("workspace_bytes", ctypes.c_int64)]
@@ -217,7 +217,7 @@ def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, 
     ``sm_scale`` defaults to ``head_dim ** -0.5``; ``max_qo_len`` defaults to
     the shape-only bound ``T - (B - 1)``; ``chunk_keys`` -1 lets the planner
     choose the prefix split, 0 forces one work item per request (direct
-    output), a positive multiple of 64 forces that chunk length.
+    output), a positive multiple of 16 forces that chunk length.
     """
     lib = load()
     problem, sm, out, lse, workspace, ws_bytes = _prepare(

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvat.so")
 ARCH = "gfx950"
 
-SOURCES = ["plan.cpp", "kernels.hip", "api.hip"]
+SOURCES = ["plan.cpp", "tile_kernel.hip", "stream_kernel.hip", "merge_kernel.hip", "api.hip"]
 
 
 def hipcc() -> str:
@@ -35,6 +35,7 @@ def hipcc() -> str:
 def common_flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wall", "-Wno-unused-function"]
 
 

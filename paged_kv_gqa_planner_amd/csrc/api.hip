@@ -9,7 +9,8 @@
 #include "verify_attention.h"
 
 namespace vat {
-const void* partial_kernel(int kv_dtype, int head_dim, int rt);
+const void* tile_kernel(int kv_dtype, int head_dim, int rt);
+const void* stream_kernel(int kv_dtype, int head_dim, int rt);
 const void* merge_kernel(int q_is_f32, int head_dim);
 }  // namespace vat
 
@@ -123,11 +124,11 @@ vat_status_t launch_partial(const vat_problem_t* p, const vat_plan_t& plan, cons
   a.row_blocks = plan.row_blocks;
   a.waves_rows = plan.waves_rows;
   a.waves_keys = plan.waves_keys;
-  a.direct = plan.direct;
-  a.chunk_keys = plan.direct ? 1 : plan.chunk_keys;
+  a.chunk_keys = plan.chunk_keys;
   a.num_ids = plan.num_chunk_ids;
   a.has_mask = p->has_mask;
-  const void* fn = vat::partial_kernel(p->kv_dtype, p->head_dim, plan.row_tiles_per_wave);
+  const void* fn = plan.kernel ? vat::stream_kernel(p->kv_dtype, p->head_dim, plan.rows_per_block / 16)
+                               : vat::tile_kernel(p->kv_dtype, p->head_dim, plan.row_tiles_per_wave);
   if (plan.lds_bytes > 65536) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, plan.lds_bytes) !=
         hipSuccess)

@@ -1,8 +1,10 @@
 // Shape-only planner: reads sizes, never device memory, so a call can be
-// captured into a HIP graph. Its job follows the split planner of the
-// flashmap page "sglang/verify_attention.py" (SplitKVVerify.splits and
-// row_blocks): pick row blocks that hold all G*L query rows of one KV head,
-// and split the prefix so that the batch fills every compute unit.
+// captured into a HIP graph. It follows the split planner of the flashmap
+// page "sglang/verify_attention.py" (SplitKVVerify.splits and row_blocks):
+// hold all G*L query rows of a KV head together so each key is read once per
+// KV head, and split the keys so the batch fills every compute unit -- here
+// with chunks of a fixed length sized from the page-table capacity, so long
+// and short requests get work items of the same size.
 #include "plan.h"
 
 #include <string.h>
@@ -13,13 +15,9 @@ namespace {
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
-int ilog2(int64_t x) {
-  int s = 0;
-  while ((int64_t(1) << s) < x) ++s;
-  return s;
-}
-
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t elem_bytes(int32_t dtype) { return dtype == VAT_F32 ? 4 : (dtype == VAT_BF16 ? 2 : 1); }
 
 }  // namespace
 
@@ -70,28 +68,49 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   }
   if (R > int64_t(INT32_MAX) / 2) return VAT_ERR_SHAPE;
   plan->rows = int32_t(R);
-
-  // Row tiling. A wave holds RT 16-row MFMA tiles of the row block; waves
-  // split the rows (waves_rows) and, when rows are few, the keys (waves_keys),
-  // so the workgroup's four waves stay busy at any G*L.
   const int64_t tiles = cdiv(R, 16);
-  int rt, wr;
-  if (tiles <= 3) {
+  const int64_t D = p->head_dim;
+  const int64_t eb = elem_bytes(p->kv_dtype);
+
+  // Kernel and row tiling.
+  //  * Streaming kernel (bf16 / fp8 caches, at most six 16-row tiles per KV
+  //    head -- every verify shape): one row block; each group of four waves
+  //    splits a 64-key stage into 16-key tiles, and the two groups split the
+  //    row tiles (or alternate stages when there is one tile), so each key is
+  //    read from HBM once and from LDS once or twice.
+  //  * Row-tiled kernel (fp32 caches, wider row sets such as prefill): a wave
+  //    holds RT tiles; waves split the rows and, when rows are few, the keys.
+  int rt, wr, wk;
+  // fp8 caches with D = 64 have too few 1 KB loads per stage for eight waves.
+  const bool stream = (p->kv_dtype != VAT_F32) && tiles <= kStreamMaxTiles &&
+                      !(p->kv_dtype == VAT_FP8_E4M3FN && p->head_dim == 64);
+  if (stream) {
+    // One row tile: both wave groups hold it and take alternate stages.
+    // Otherwise the two groups split ceil(tiles / 2) tiles each.
+    rt = tiles == 1 ? 1 : int(cdiv(tiles, 2));
+    wr = tiles == 1 ? 1 : 2;
+    wk = tiles == 1 ? 2 * kWaves : kWaves;
+  } else if (tiles <= 3) {
     rt = int(tiles);
     wr = 1;
+    wk = kWaves;
   } else if (tiles == 4) {
     rt = 2;
     wr = 2;
+    wk = 2;
   } else if (tiles <= 6) {
     rt = 3;
     wr = 2;
+    wk = 2;
   } else {
     rt = 2;
     wr = 4;
+    wk = 1;
   }
-  const int wk = kWaves / wr;
   const int64_t M = int64_t(wr) * rt * 16;
   const int64_t RB = cdiv(R, M);
+  plan->kernel = stream ? 1 : 0;
+  plan->threads = stream ? kStreamThreads : kThreads;
   plan->row_tiles_per_wave = rt;
   plan->waves_rows = wr;
   plan->waves_keys = wk;
@@ -99,64 +118,85 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   plan->row_blocks = int32_t(RB);
   if (int64_t(p->num_kv_heads) * RB > 65535) return VAT_ERR_UNSUPPORTED;
 
-  // Split or not. Without a split each (request, KV head, row block) is one
-  // workgroup that writes the output itself; that is enough work items when
-  // they already cover the chip several times over. Otherwise the prefix is
-  // cut into fixed-length chunks (plus one item per request for the draft
-  // block), sized from the page-table capacity so the chunk count fills the
-  // compute units; a later merge combines them.
-  const int64_t base_items = int64_t(p->batch) * p->num_kv_heads * RB;
-  bool direct;
-  int64_t ck = 0;
-  if (p->chunk_keys == 0) {
-    direct = true;
-  } else if (p->chunk_keys > 0) {
-    direct = false;
-    ck = p->chunk_keys;
+  // LDS. Streaming: a ring of 64-key stages (K and V), as many as fit the
+  // budget (2..8), plus the chunk's page ids; the four waves' final combine
+  // reuses it. Row-tiled: a
+  // per-wave 32-key V staging tile (bf16 after any fp8 decode) and the slots
+  // of the key-splitting waves' combine.
+  const int64_t ndt = D / 16;
+  if (stream) {
+    const int64_t stage = 2 * kStageKeys * D * eb;
+    int64_t ns = kStreamLdsBudget / stage;
+    if (ns > 8) ns = 8;
+    if (ns < 2) ns = 2;
+    plan->stages = int32_t(ns);
+    const int64_t ring = ns * stage + kStreamPageWindow * 4;
+    // Combine slots: four per row set (eight waves on one tile) or two per
+    // group (two groups of four waves).
+    const int64_t combine = 4 * (int64_t(rt) * ndt * 256 + int64_t(rt) * 32) * 4;
+    plan->lds_bytes = int32_t(ring > combine ? ring : combine);
   } else {
-    direct = base_items >= 4 * int64_t(num_cus);
-    if (!direct) {
-      const int64_t total_keys = int64_t(p->num_kv_indices) * p->page_size;
-      const int64_t target = 4 * int64_t(num_cus);
-      int64_t slots = target - 2 * base_items;
-      if (slots < num_cus) slots = num_cus;
-      ck = cdiv(total_keys * p->num_kv_heads * RB, slots);
-      ck = cdiv(ck, kChunkQuantum) * kChunkQuantum;
-      if (ck < kMinChunkKeys) ck = kMinChunkKeys;
-    }
+    const int64_t lds_v = (p->kv_dtype == VAT_F32) ? 0 : int64_t(kWaves) * kStepKeys * D * 2;
+    int64_t lds_c = 0;
+    if (wk > 1) lds_c = int64_t(wk / 2) * wr * (int64_t(rt) * ndt * 256 + int64_t(rt) * 32) * 4;
+    plan->lds_bytes = int32_t(lds_v > lds_c ? lds_v : lds_c);
   }
-  plan->direct = direct ? 1 : 0;
-  const int64_t ndt = p->head_dim / 16;
-  // LDS: per-wave staging of one step's V tile (bf16 after any fp8 decode),
-  // and the slots the key-splitting waves use to combine their partials.
-  int64_t lds_v = (p->kv_dtype == VAT_F32) ? 0 : int64_t(kWaves) * kStepKeys * p->head_dim * 2;
-  int64_t lds_c = 0;
-  if (wk > 1) lds_c = int64_t(wk / 2) * wr * (int64_t(rt) * ndt * 256 + int64_t(rt) * 32) * 4;
-  plan->lds_bytes = int32_t(lds_v > lds_c ? lds_v : lds_c);
   if (plan->lds_bytes > 160 * 1024) return VAT_ERR_UNSUPPORTED;
 
-  if (direct) {
-    plan->chunk_keys = 0;
-    plan->num_chunk_ids = 0;
-    plan->grid_x = p->batch;
-    plan->grid_y = int32_t(p->num_kv_heads * RB);
-    plan->merge_grid = 0;
-    plan->workspace_bytes = 0;
-    return VAT_OK;
-  }
+  // Chunk length. Each request's keys [0, kv_len) form ceil(kv_len / C)
+  // work items (the draft block is masked inside the last one); a request
+  // with one item writes its output directly, the others go through the
+  // log-sum-exp merge. The planner sizes C from the page-table capacity so
+  // that the items about fill the compute units once (the streaming kernel
+  // holds one workgroup per CU), within [kMinChunkKeys, kMaxChunkKeys]; a
+  // row-tiled plan whose (request, KV head, row block) items already cover
+  // the chip four times over is not split at all.
   const int64_t total_keys = int64_t(p->num_kv_indices) * p->page_size;
-  const int64_t ids = total_keys / ck + 2 * int64_t(p->batch);
+  const int64_t whole = cdiv(total_keys > 0 ? total_keys : 1, kChunkQuantum) * kChunkQuantum;
+  const int64_t base_items = int64_t(p->batch) * p->num_kv_heads * RB;
+  int64_t ck;
+  if (p->chunk_keys == 0) {
+    ck = whole;
+  } else if (p->chunk_keys > 0) {
+    ck = p->chunk_keys;
+  } else if (!stream && base_items >= 4 * int64_t(num_cus)) {
+    ck = whole;
+  } else if (stream) {
+    // Split the average request evenly into as many chunks as leave one
+    // workgroup per CU: with equal request lengths every chunk then has the
+    // same length and the items fill the CUs exactly once.
+    const int64_t per_req = cdiv(total_keys, p->batch);
+    int64_t nchunk = int64_t(num_cus) / (int64_t(p->batch) * p->num_kv_heads * RB);
+    if (nchunk < 1) nchunk = 1;
+    ck = cdiv(cdiv(per_req, nchunk), kChunkQuantum) * kChunkQuantum;
+    if (ck < kMinChunkKeys) ck = kMinChunkKeys;
+    if (ck > kMaxChunkKeys) ck = kMaxChunkKeys;
+  } else {
+    ck = cdiv(total_keys * p->num_kv_heads * RB, 4 * int64_t(num_cus));
+    ck = cdiv(ck, kChunkQuantum) * kChunkQuantum;
+    if (ck < kMinChunkKeys) ck = kMinChunkKeys;
+    if (ck > kMaxChunkKeys) ck = kMaxChunkKeys;
+  }
+  if (ck > int64_t(INT32_MAX) / 2) return VAT_ERR_UNSUPPORTED;
+  const bool direct = ck >= total_keys;
+  const int64_t ids = total_keys / ck + p->batch;
   if (ids > int64_t(INT32_MAX)) return VAT_ERR_UNSUPPORTED;
+  plan->direct = direct ? 1 : 0;
   plan->chunk_keys = int32_t(ck);
   plan->num_chunk_ids = int32_t(ids);
   plan->grid_x = int32_t(ids);
   plan->grid_y = int32_t(p->num_kv_heads * RB);
+  if (direct) {
+    plan->merge_grid = 0;
+    plan->workspace_bytes = 0;
+    return VAT_OK;
+  }
   const int64_t row_groups = cdiv(M, kMergeRows);
   const int64_t mg = base_items * row_groups;
   if (mg > int64_t(INT32_MAX)) return VAT_ERR_UNSUPPORTED;
   plan->merge_grid = int32_t(mg);
   const int64_t parts = ids * p->num_kv_heads * RB;
-  const int64_t o_bytes = parts * M * p->head_dim * 4;
+  const int64_t o_bytes = parts * M * D * 4;
   const int64_t lse_off = cdiv(o_bytes, 256) * 256;
   plan->workspace_bytes = lse_off + cdiv(parts * M * 4, 256) * 256;
   return VAT_OK;

@@ -8,23 +8,33 @@
 
 namespace vat {
 
-// Keys each wave consumes per step of its key loop (two 16-key MFMA tiles).
-constexpr int kStepKeys = 32;
 // Threads per partial-kernel workgroup: four wave64s.
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-// Query rows merged per merge-kernel workgroup.
+// Row-tiled kernel: keys each wave consumes per step (two 16-key MFMA tiles).
+constexpr int kStepKeys = 32;
+// Streaming kernel: eight waves (two groups of four); keys per LDS stage (one
+// 16-key MFMA tile per wave of a group), most query rows per KV head it takes
+// (six 16-row tiles, three per group), LDS its stage ring may fill.
+constexpr int kStreamThreads = 512;
+constexpr int kStageKeys = 64;
+constexpr int kStreamMaxTiles = 6;
+constexpr int kStreamLdsBudget = 128 * 1024;
+// Page ids the streaming kernel keeps in LDS at a time.
+constexpr int kStreamPageWindow = 2048;
+// Query rows merged per merge-kernel workgroup (one wave per row).
 constexpr int kMergeRows = 4;
 constexpr int kMergeThreads = 256;
-// Smallest prefix chunk the planner picks, in keys.
-constexpr int kMinChunkKeys = 256;
-// Prefix chunks are multiples of this many keys.
-constexpr int kChunkQuantum = 64;
+// Chunk lengths the planner picks are multiples of kChunkQuantum within
+// [kMinChunkKeys, kMaxChunkKeys].
+constexpr int kChunkQuantum = 16;
+constexpr int kMinChunkKeys = 128;
+constexpr int kMaxChunkKeys = 2048;
 // Largest draft count per request a bit-packed mask may carry (one 64-bit
 // register holds a row).
 constexpr int kMaxMaskedLen = 64;
 
-// Arguments of the partial kernel; every field is a plain pointer or integer.
+// Arguments of both partial kernels; every field is a plain pointer or integer.
 struct PartialArgs {
   const void* q;
   const void* k_cache;
@@ -44,7 +54,7 @@ struct PartialArgs {
   int32_t batch, hq, hkv, group, tokens;
   int32_t page_shift, num_pages, num_kv_indices, num_mask_bytes;
   int32_t rows_per_block, row_blocks, waves_rows, waves_keys;
-  int32_t direct, chunk_keys, num_ids, has_mask;
+  int32_t chunk_keys, num_ids, has_mask;
 };
 
 // Arguments of the merge kernel.

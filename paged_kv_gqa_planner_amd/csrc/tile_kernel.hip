@@ -1,151 +1,26 @@
-// gfx950 kernels for verification attention over a paged KV cache.
+// Row-tiled partial kernel: fp32 caches and wide row sets (prefill).
 //
-// vat_partial: one workgroup (four wave64s) per (work item, KV head, row
+// One workgroup (four wave64s) per (chunk of a request's keys, KV head, row
 // block). A row block holds query rows r = t * G + g (token-major) of the
 // request's G * L_b rows that share KV head h, so every key and value of the
-// item is fetched once per KV head and row block rather than once per query
+// chunk is fetched once per KV head and row block rather than once per query
 // head (flashmap page "sglang/verify_attention.py", module docstring and
-// _verify_partial_kernel). A work item is either a chunk of the request's
-// prefix (all rows see all of it), the request's draft block (keys
-// prefix_b .. kv_len_b, under the causal rule or the bit-packed mask), or,
-// in direct mode, the whole key range with the output written in place.
+// _verify_partial_kernel). The draft block at the end of the request is
+// masked in place (causal or bit-packed tree mask); rows of a causal row
+// block stop at their last token's key.
 //
 // Inner step (32 keys per wave): keys are gathered through the page table
 // straight into MFMA operand registers with 16-byte loads; logits are
-// computed transposed, S^T = K . Q^T (v_mfma_f32_16x16x32_bf16), so that each
-// lane owns one query row and its exponentiated logits are already laid out
-// as the B operand of O^T = V^T . P^T. V goes through a per-wave LDS tile
+// computed transposed, S^T = K . Q^T (v_mfma_f32_16x16x32_bf16, or
+// v_mfma_f32_16x16x4f32 for fp32), so that each lane owns one query row and
+// its exponentiated logits are already laid out as the B operand of
+// O^T = V^T . P^T. For bf16/fp8 caches V goes through a per-wave LDS tile
 // (XOR-swizzled 16-byte chunks) to be read back transposed. The online
 // softmax keeps a running max and sum per row in base 2 (the scale
 // sm_scale * k_scale * log2 e is folded into one FMA before v_exp_f32).
-//
-// vat_merge: combines a request's partials by their log-sum-exp (flashmap
-// page, _verify_merge_kernel) and writes out and the natural-log lse.
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include "plan.h"
+#include "device_common.h"
 
 namespace vat {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-enum { KV_F32 = 0, KV_BF16 = 1, KV_E4M3 = 2 };
-
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kNegInf = -__builtin_huge_valf();
-
-__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
-
-// Max / sum over the four lanes l, l^16, l^32, l^48 that hold the same row.
-__device__ __forceinline__ float row_max4(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-__device__ __forceinline__ float row_sum4(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
-
-// Two fp8 e4m3fn codes (bytes 0,1 or 2,3 of `w`) -> two bf16, exactly. The
-// packed result is read back as one 32-bit word: extracting single elements
-// of this builtin's vector result is mis-lowered by the compiler.
-__device__ __forceinline__ unsigned e4m3x2_lo(unsigned w) {
-  bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false);
-  return __builtin_bit_cast(unsigned, r);
-}
-__device__ __forceinline__ unsigned e4m3x2_hi(unsigned w) {
-  bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true);
-  return __builtin_bit_cast(unsigned, r);
-}
-// 8 fp8 codes (two dwords) -> 8 bf16 (four dwords).
-__device__ __forceinline__ u32x4 e4m3x8_to_bf16(unsigned a, unsigned b) {
-  u32x4 r;
-  r.x = e4m3x2_lo(a);
-  r.y = e4m3x2_hi(a);
-  r.z = e4m3x2_lo(b);
-  r.w = e4m3x2_hi(b);
-  return r;
-}
-
-__device__ __forceinline__ unsigned f32_to_bf16_bits(float f) {
-  // Round to nearest even; NaN stays NaN.
-  unsigned u = __builtin_bit_cast(unsigned, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
-
-// Request geometry, every value clamped into range.
-struct Req {
-  int kv_start;  // first index into kv_indices
-  int pages;
-  int kv_len;
-  int L;         // query tokens
-  int prefix;    // kv_len - L
-  int q_start;   // first query row
-};
-
-template <class A>
-__device__ __forceinline__ Req load_req(const A& a, int b) {
-  Req r;
-  const int ip0 = clampi(a.kv_indptr[b], 0, a.num_kv_indices);
-  const int ip1 = clampi(a.kv_indptr[b + 1], ip0, a.num_kv_indices);
-  r.kv_start = ip0;
-  r.pages = ip1 - ip0;
-  const int ps = 1 << a.page_shift;
-  const int lp = clampi(a.last_page_len[b], 1, ps);
-  r.kv_len = r.pages > 0 ? ((r.pages - 1) << a.page_shift) + lp : 0;
-  const int q0 = clampi(a.qo_indptr[b], 0, a.tokens);
-  const int q1 = clampi(a.qo_indptr[b + 1], q0, a.tokens);
-  r.L = min(q1 - q0, r.kv_len);
-  r.q_start = q0;
-  r.prefix = r.kv_len - r.L;
-  return r;
-}
-
-// First chunk id of request b in split mode. Ids of request b are
-// start_b .. start_b + ceil(prefix_b / chunk) (the last one is the draft
-// block); start_b = floor(kv_indptr[b] * page_size / chunk) + 2 b keeps the
-// ranges of consecutive requests disjoint and below
-// floor(num_kv_indices * page_size / chunk) + 2 B.
-__device__ __forceinline__ int chunk_start(int ip0, int page_shift, int chunk, int b) {
-  return (int)(((long long)ip0 << page_shift) / chunk) + 2 * b;
-}
-
-// Request owning chunk id c: the last b with start_b <= c, found by a
-// 64-way search (each round narrows the range 64-fold). Wave-uniform.
-__device__ __forceinline__ int find_request(const PartialArgs& a, int c, int lane) {
-  int lo = 0, hi = a.batch;
-  while (hi - lo > 1) {
-    const int span = hi - lo;
-    const int step = (span + 63) / 64;
-    const int bb = lo + lane * step;
-    bool ok = false;
-    if (bb < hi) {
-      const int ip = clampi(a.kv_indptr[bb], 0, a.num_kv_indices);
-      ok = chunk_start(ip, a.page_shift, a.chunk_keys, bb) <= c;
-    }
-    const unsigned long long m = __ballot(ok);
-    const int cnt = __popcll(m);
-    if (cnt == 0) return -1;
-    lo = lo + (cnt - 1) * step;
-    hi = min(hi, lo + step);
-  }
-  return lo;
-}
 
 // ---------------------------------------------------------------------------
 // Page-id window: lane i of a wave holds the page id of request page
@@ -527,41 +402,27 @@ __global__ __launch_bounds__(kThreads) void vat_partial(PartialArgs a) {
   const int y = blockIdx.y;
   const int h = y % a.hkv;
   const int rb = a.row_blocks - 1 - y / a.hkv;  // heaviest (latest tokens) first
-  int b, cid = 0;
-  if (a.direct) {
-    b = blockIdx.x;
-  } else {
-    cid = blockIdx.x;
-    b = find_request(a, cid, lane);
-    if (b < 0) return;
-  }
-  const Req r = load_req(a, b);
+  const int cid = blockIdx.x;
+  ReqArrays ra{a.kv_indptr, a.last_page_len, a.qo_indptr, a.has_mask ? a.mask_indptr : nullptr,
+               a.batch, a.page_shift, a.chunk_keys, a.num_kv_indices, a.tokens};
+  Req r;
+  Item it;
+  if (!find_item(ra, cid, lane, r, it)) return;
+  const int n_items = chunk_count(r.kv_len, a.chunk_keys);
+  const int j = it.j;
   const int R = a.group * r.L;
   const int row0 = rb * a.rows_per_block;
   if (row0 >= R) return;
   const int t_hi = (min(row0 + a.rows_per_block, R) - 1) / a.group;
 
-  // Key range of this work item.
-  int lo, hi;
+  // Key range of this work item: chunk j of the request's keys; a causal row
+  // block needs nothing past its last token's own key.
+  const int lo = j * a.chunk_keys;
+  int hi = min(lo + a.chunk_keys, r.kv_len);
+  if (!a.has_mask) hi = min(hi, r.prefix + t_hi + 1);
   Vis vis;
   vis.has_mask = a.has_mask;
   vis.masked_from = r.prefix;
-  if (a.direct) {
-    lo = 0;
-    hi = a.has_mask ? r.kv_len : r.prefix + t_hi + 1;
-  } else {
-    const int ip0 = r.kv_start;
-    const int j = cid - chunk_start(ip0, a.page_shift, a.chunk_keys, b);
-    const int npre = (r.prefix + a.chunk_keys - 1) / a.chunk_keys;
-    if (j < 0 || j > npre) return;
-    if (j < npre) {
-      lo = j * a.chunk_keys;
-      hi = min(lo + a.chunk_keys, r.prefix);
-    } else {
-      lo = r.prefix;
-      hi = a.has_mask ? r.kv_len : r.prefix + t_hi + 1;
-    }
-  }
   vis.hi = hi;
   const int last = max(hi - 1, 0);
 
@@ -577,26 +438,8 @@ __global__ __launch_bounds__(kThreads) void vat_partial(PartialArgs a) {
     row_g[rt] = row % a.group;
     row_ok[rt] = row < R;
     row_bits[rt] = 0;
-    if (a.has_mask && row_ok[rt]) {
-      // Row t's L bits start at bit t * L of the request's segment.
-      const int seg = a.mask_indptr[b];
-      const int bit0 = row_t[rt] * r.L;
-      const int nbytes = ((bit0 & 7) + r.L + 7) >> 3;
-      unsigned long long acc_bits = 0;
-      for (int i = nbytes - 1; i >= 0; --i) {
-        const int idx = clampi(seg + (bit0 >> 3) + i, 0, max(a.num_mask_bytes - 1, 0));
-        acc_bits = (acc_bits << 8) | (unsigned long long)a.mask[idx];
-      }
-      // nbytes <= 9 for L <= 64: the ninth byte's bits land above bit 63 of
-      // the shifted value; fetch them separately.
-      unsigned long long bits = acc_bits >> (bit0 & 7);
-      if (nbytes == 9) {
-        const int idx = clampi(seg + (bit0 >> 3) + 8, 0, max(a.num_mask_bytes - 1, 0));
-        bits |= (unsigned long long)a.mask[idx] << (64 - (bit0 & 7));
-      }
-      if (r.L < 64) bits &= (1ull << r.L) - 1ull;
-      row_bits[rt] = bits;
-    }
+    if (a.has_mask && row_ok[rt])
+      row_bits[rt] = load_mask_row(a.mask, a.num_mask_bytes, r.mask_off, row_t[rt], r.L);
   }
 
   // Q^T operand fragments.
@@ -710,7 +553,8 @@ __global__ __launch_bounds__(kThreads) void vat_partial(PartialArgs a) {
 
   // Write: direct -> out (q dtype) and natural-log lse; split -> fp32 partial
   // (normalised, v_scale not yet applied) and base-2 lse.
-  const int pid = a.direct ? 0 : ((cid * a.hkv + h) * a.row_blocks + rb);
+  const bool final_write = n_items == 1;
+  const long long pid = ((long long)it.slot * a.hkv + h) * a.row_blocks + rb;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     if (!row_ok[rt]) continue;
@@ -718,7 +562,7 @@ __global__ __launch_bounds__(kThreads) void vat_partial(PartialArgs a) {
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     const float lse2 = lsum > 0.f ? acc.m[rt] + fast_log2(lsum) : kNegInf;
     const int local = (wr * RT + rt) * 16 + l16;
-    if (a.direct) {
+    if (final_write) {
       const long long orow =
           ((long long)(r.q_start + row_t[rt]) * a.hq + h * a.group + row_g[rt]) * D;
       const float sc = inv * a.v_scale;
@@ -748,89 +592,7 @@ __global__ __launch_bounds__(kThreads) void vat_partial(PartialArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge: one workgroup per (request, KV head, row block, group of kMergeRows
-// rows); 64 threads per row, each owning D / 64 consecutive head dims.
-template <int QF32, int D>
-__global__ __launch_bounds__(kMergeThreads) void vat_merge(MergeArgs a) {
-  constexpr int PER = D / 64;
-  const int tid = threadIdx.x;
-  const int lr = tid >> 6;        // row within the group
-  const int lane = tid & 63;
-  int x = blockIdx.x;
-  const int rg = x % a.row_groups;
-  x /= a.row_groups;
-  const int rb = x % a.row_blocks;
-  x /= a.row_blocks;
-  const int h = x % a.hkv;
-  const int b = x / a.hkv;
-  Req r;
-  {
-    const int ip0 = clampi(a.kv_indptr[b], 0, a.num_kv_indices);
-    const int ip1 = clampi(a.kv_indptr[b + 1], ip0, a.num_kv_indices);
-    r.kv_start = ip0;
-    r.pages = ip1 - ip0;
-    const int ps = 1 << a.page_shift;
-    const int lp = clampi(a.last_page_len[b], 1, ps);
-    r.kv_len = r.pages > 0 ? ((r.pages - 1) << a.page_shift) + lp : 0;
-    const int q0 = clampi(a.qo_indptr[b], 0, a.tokens);
-    const int q1 = clampi(a.qo_indptr[b + 1], q0, a.tokens);
-    r.L = min(q1 - q0, r.kv_len);
-    r.q_start = q0;
-    r.prefix = r.kv_len - r.L;
-  }
-  const int local = rg * kMergeRows + lr;
-  const int row = rb * a.rows_per_block + local;
-  if (local >= a.rows_per_block || row >= a.group * r.L) return;
-  const int t = row / a.group, g = row % a.group;
-  const int first = chunk_start(r.kv_start, a.page_shift, a.chunk_keys, b);
-  const int items = (r.prefix + a.chunk_keys - 1) / a.chunk_keys + 1;
-  float m = kNegInf, den = 0.f;
-  float o[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) o[i] = 0.f;
-  for (int it = 0; it < items; ++it) {
-    const int cid = min(first + it, a.num_ids - 1);
-    const long long pid = ((long long)cid * a.hkv + h) * a.row_blocks + rb;
-    const float ls = a.part_lse[pid * a.rows_per_block + local];
-    if (ls == kNegInf) continue;
-    const float m_new = fmaxf(m, ls);
-    const float alpha = fast_exp2(m - m_new);
-    const float w = fast_exp2(ls - m_new);
-    const float* po = a.part_o + (pid * a.rows_per_block + local) * D + lane * PER;
-    float v[PER];
-    if constexpr (PER == 2) {
-      const float2 x2 = *(const float2*)po;
-      v[0] = x2.x;
-      v[1] = x2.y;
-    } else {
-      v[0] = po[0];
-    }
-#pragma unroll
-    for (int i = 0; i < PER; ++i) o[i] = o[i] * alpha + v[i] * w;
-    den = den * alpha + w;
-    m = m_new;
-  }
-  const long long orow = (long long)(r.q_start + t) * a.hq + h * a.group + g;
-  const float sc = den > 0.f ? a.v_scale / den : 0.f;
-  if constexpr (QF32) {
-    float* op = (float*)a.out + orow * D + lane * PER;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) op[i] = o[i] * sc;
-  } else {
-    unsigned short* op = (unsigned short*)a.out + orow * D + lane * PER;
-    if constexpr (PER == 2) {
-      *(unsigned*)op = pack_bf16x2(o[0] * sc, o[1] * sc);
-    } else {
-      op[0] = (unsigned short)f32_to_bf16_bits(o[0] * sc);
-    }
-  }
-  if (lane == 0) a.lse[orow] = den > 0.f ? (m + fast_log2(den)) * kLn2 : kNegInf;
-}
-
-// ---------------------------------------------------------------------------
-// Host-side launch table (used by api.hip).
 typedef void (*PartialFn)(PartialArgs);
-typedef void (*MergeFn)(MergeArgs);
 
 template <int KV, int D>
 static PartialFn pick_rt(int rt) {
@@ -841,15 +603,10 @@ static PartialFn pick_rt(int rt) {
   }
 }
 
-const void* partial_kernel(int kv_dtype, int head_dim, int rt) {
+const void* tile_kernel(int kv_dtype, int head_dim, int rt) {
   if (kv_dtype == KV_F32) return (const void*)(head_dim == 64 ? pick_rt<KV_F32, 64>(rt) : pick_rt<KV_F32, 128>(rt));
   if (kv_dtype == KV_BF16) return (const void*)(head_dim == 64 ? pick_rt<KV_BF16, 64>(rt) : pick_rt<KV_BF16, 128>(rt));
   return (const void*)(head_dim == 64 ? pick_rt<KV_E4M3, 64>(rt) : pick_rt<KV_E4M3, 128>(rt));
-}
-
-const void* merge_kernel(int q_is_f32, int head_dim) {
-  if (q_is_f32) return (const void*)(head_dim == 64 ? vat_merge<1, 64> : vat_merge<1, 128>);
-  return (const void*)(head_dim == 64 ? vat_merge<0, 64> : vat_merge<0, 128>);
 }
 
 }  // namespace vat

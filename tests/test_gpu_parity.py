@@ -60,7 +60,7 @@ def _fuzz_case(seed):
     Lmax = 20 if mask_kind != "causal" else 40
     lens = [int(x) for x in rng.integers(1, Lmax + 1, size=B)]
     prefixes = [int(x) for x in rng.integers(0, 301, size=B)]
-    chunk = int(rng.choice([-1, 0, 64, 128]))
+    chunk = int(rng.choice([-1, 0, 48, 64, 128]))
     p = make_case(seed, prefix_lens=prefixes, qo_lens=lens, num_qo_heads=G * Hkv,
                   num_kv_heads=Hkv, head_dim=D, page_size=ps, q_dtype=q_dt, kv_dtype=kv_dt,
                   mask_kind=mask_kind, fp8_absmax_scales=(kv_dt == "e4m3"), mask_density=0.4,
@@ -179,7 +179,7 @@ def test_repeat_runs_are_bitwise_identical(gpu_lib):
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("chunk", [0, 64, 128, 256, 512, 2048])
+@pytest.mark.parametrize("chunk", [0, 16, 64, 112, 256, 528, 2048])
 def test_any_split_matches_oracle(gpu_lib, chunk):
     p = make_config(3, prefix=4096)
     say(f"[split chunk={chunk}]")
