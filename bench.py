@@ -12,9 +12,10 @@ Before timing, the output of every copy is checked: copy 0 against the CPU
 oracle at the parity tolerances, the others bitwise against copy 0. The
 timed K steps run back to back on one stream; the stream is first held by a
 short GPU sleep so that the host has queued all K steps before the first
-one starts and HIP events measure GPU time only. Events around each partial
-kernel give its average duration, from which the roofline fraction is
-computed with the algorithmic bytes (KV-bound workloads) or FLOPs (prefill).
+one starts and HIP events measure GPU time only. A second run of K partial
+kernels alone, timed the same way, gives that kernel's average duration,
+from which the roofline fraction is computed with the algorithmic bytes
+(KV-bound workloads) or FLOPs (prefill).
 
 Prints one JSON line. The oracle (single-threaded NumPy float64) is timed on
 the host on the same workload as the ``cpu_baseline`` leg.
@@ -113,6 +114,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum host time spent timing the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run K device-to-device copies of MIB MiB (for scaling HBM "
+                         "byte counters) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -132,6 +136,17 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        # A plain copy of known size: reads and writes exactly n bytes each.
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": args.steps}), flush=True)
+        return
 
     p = make_config(args.config, prefix=args.prefix)
     kvb, flops = algorithmic_work(p)
@@ -199,13 +214,11 @@ def main():
         batches[i % copies]()
     torch.cuda.synchronize()
 
-    # ---- timed region
+    # ---- timed region: K whole steps back to back, then (for the roofline)
+    # K partial-kernel launches back to back, each bracketed by two events.
+    # Before each run the stream is held by a GPU sleep long enough for the
+    # host to queue every launch, so the events time GPU work only.
     K = args.steps
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    # Calibrate the GPU sleep that holds the stream while the host queues K steps.
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     c0.record()
     torch.cuda._sleep(1_000_000)
@@ -219,27 +232,31 @@ def main():
     host_per_step = (time.perf_counter() - t_host) / 3
     torch.cuda.synchronize()
     hold_ms = 20.0 + 2.0 * K * host_per_step * 1e3
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(hold_ms * cycles_per_ms))
-    start.record()
-    t_enq = time.perf_counter()
-    for i in range(K):
-        call = batches[i % copies]
-        ev_a[i].record()
-        call.partial()
-        ev_b[i].record()
-        call.merge()
-    end.record()
-    enqueue_ms = (time.perf_counter() - t_enq) * 1e3
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    partial_ms = [ev_a[i].elapsed_time(ev_b[i]) for i in range(K)]
-    gpu_ran_ahead = enqueue_ms < hold_ms
 
+    def timed(launch):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(hold_ms * cycles_per_ms))
+        start.record()
+        t_enq = time.perf_counter()
+        for i in range(K):
+            launch(batches[i % copies])
+        end.record()
+        enqueue_ms = (time.perf_counter() - t_enq) * 1e3
+        torch.cuda.synchronize()
+        return start.elapsed_time(end), enqueue_ms < hold_ms
+
+    def step(call):
+        call.partial()
+        call.merge()
+
+    total_ms, ahead_steps = timed(step)
+    partial_total_ms, ahead_partial = timed(lambda call: call.partial())
+    gpu_ran_ahead = ahead_steps and ahead_partial
     ms_per_step = total_ms / K
     value = tokens * K / (total_ms * 1e-3)
-    part_avg = float(np.mean(partial_ms))
-    part_med = float(np.median(partial_ms))
+    part_avg = partial_total_ms / K
     plan = batches[0].plan.as_dict()
     if args.config == 4:
         achieved = flops / (part_avg * 1e-3) / 1e12
@@ -280,8 +297,7 @@ def main():
         "kv_read_gbps_step": round(kvb / (ms_per_step * 1e-3) / 1e9, 1),
         "kv_frac_of_peak_step": round(kvb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": roof,
-        "partial_kernel_ms": {"mean": round(part_avg, 5), "median": round(part_med, 5),
-                              "min": round(float(np.min(partial_ms)), 5)},
+        "partial_kernel_ms": round(part_avg, 5),
         "verified": bool(verified),
         "parity": {"max_out_err": err_o, "max_lse_err": err_l,
                    "tol_out": TOL_OUT[p.q_dtype], "tol_lse": TOL_LSE,

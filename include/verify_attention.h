@@ -113,6 +113,10 @@ typedef struct {
   int32_t kernel;           /* 1: LDS-ring streaming kernel (bf16/fp8 KV, <= 80
                                query rows per KV head); 0: row-tiled kernel */
   int32_t stages;           /* streaming kernel: 64-key stages in flight in LDS */
+  int32_t slices;           /* > 0: balanced scheduling. Per KV head, the requests'
+                               keys (each padded to 16) are laid end to end and cut
+                               into `slices` equal ranges, one workgroup each; 0:
+                               each request is cut into chunk_keys-long chunks */
   int32_t group;            /* G = Hq / Hkv */
   int32_t rows;             /* G * max_qo_len query rows per (request, KV head) */
   int32_t row_tiles_per_wave; /* 16-row MFMA tiles each wave holds */

@@ -127,6 +127,7 @@ vat_status_t launch_partial(const vat_problem_t* p, const vat_plan_t& plan, cons
   a.chunk_keys = plan.chunk_keys;
   a.num_ids = plan.num_chunk_ids;
   a.has_mask = p->has_mask;
+  a.slices = plan.slices;
   const void* fn = plan.kernel ? vat::stream_kernel(p->kv_dtype, p->head_dim, plan.rows_per_block / 16)
                                : vat::tile_kernel(p->kv_dtype, p->head_dim, plan.row_tiles_per_wave);
   if (plan.lds_bytes > 65536) {
@@ -167,6 +168,7 @@ vat_status_t launch_merge(const vat_problem_t* p, const vat_plan_t& plan,
   a.chunk_keys = plan.chunk_keys;
   a.num_ids = plan.num_chunk_ids;
   a.row_groups = (plan.rows_per_block + vat::kMergeRows - 1) / vat::kMergeRows;
+  a.slices = plan.slices;
   const void* fn = vat::merge_kernel(p->q_dtype == VAT_F32, p->head_dim);
   void* args[] = {&a};
   hipError_t e = hipLaunchKernel(fn, dim3(plan.merge_grid, 1, 1), dim3(plan.merge_threads, 1, 1),

@@ -4,8 +4,10 @@
 // w_i = 2^(lse_i - max lse), and the merged lse is max + log2(sum w).
 //
 // One wave per query row (each lane owns D / 64 head dims), four rows per
-// workgroup, chunks combined online eight at a time. Requests that fit one
-// chunk were written directly by the partial kernel and are skipped.
+// workgroup, partials combined online eight at a time. A request's partials
+// are its chunks (ids from chunk_start) or, with balanced slices, the slices
+// x_lo .. x_hi its keys fall in (slot x + b). Requests that fit one chunk or
+// slice were written directly by the partial kernel and are skipped.
 #include "device_common.h"
 
 namespace vat {
@@ -22,15 +24,31 @@ __global__ __launch_bounds__(kMergeThreads) void vat_merge(MergeArgs a) {
   x /= a.row_blocks;
   const int h = x % a.hkv;
   const int b = x / a.hkv;
-  const Req r = make_req(a.kv_indptr[b], a.kv_indptr[b + 1], a.last_page_len[b], a.qo_indptr[b],
-                         a.qo_indptr[b + 1], 0, a.page_shift, a.num_kv_indices, a.tokens);
-  const int n = chunk_count(r.kv_len, a.chunk_keys);
-  if (n <= 1) return;
+  ReqArrays ra{a.kv_indptr, a.last_page_len, a.qo_indptr, nullptr, a.batch, a.page_shift,
+               a.chunk_keys, a.num_kv_indices, a.tokens};
+  Req r;
+  int n, first;  // partials of request b: slots first + i, i < n
+  if (a.slices > 0) {
+    SliceLanes sl;
+    slice_lanes(ra, a.slices, lane, sl);
+    r = slice_req(ra, sl, b);
+    if (r.L == 0 || r.kv_len == 0) return;
+    const int cb = __builtin_amdgcn_readlane(sl.cum, b);
+    const int x_lo = cb / sl.per;
+    const int x_hi = (cb + r.kv_len - 1) / sl.per;
+    n = x_hi - x_lo + 1;
+    first = x_lo + b;
+  } else {
+    r = make_req(a.kv_indptr[b], a.kv_indptr[b + 1], a.last_page_len[b], a.qo_indptr[b],
+                 a.qo_indptr[b + 1], 0, a.page_shift, a.num_kv_indices, a.tokens);
+    n = chunk_count(r.kv_len, a.chunk_keys);
+    first = chunk_start(r.kv_start, a.page_shift, a.chunk_keys, b);
+  }
+  if (n <= 1) return;  // written directly by the partial kernel
   const int local = rg * kMergeRows + lr;
   const int row = rb * a.rows_per_block + local;
   if (local >= a.rows_per_block || row >= a.group * r.L) return;
   const int t = row / a.group, g = row % a.group;
-  const int first = chunk_start(r.kv_start, a.page_shift, a.chunk_keys, b);
   auto slot = [&](int i) -> long long {
     const int cid = min(first + i, a.num_ids - 1);
     return (((long long)cid * a.hkv + h) * a.row_blocks + rb) * a.rows_per_block + local;

@@ -119,8 +119,8 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   if (int64_t(p->num_kv_heads) * RB > 65535) return VAT_ERR_UNSUPPORTED;
 
   // LDS. Streaming: a ring of 64-key stages (K and V), as many as fit the
-  // budget (2..8), plus the chunk's page ids; the four waves' final combine
-  // reuses it. Row-tiled: a
+  // budget (2..8), plus the segment's page ids and the slice table; the
+  // waves' final combine reuses the ring. Row-tiled: a
   // per-wave 32-key V staging tile (bf16 after any fp8 decode) and the slots
   // of the key-splitting waves' combine.
   const int64_t ndt = D / 16;
@@ -130,7 +130,8 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
     if (ns > 8) ns = 8;
     if (ns < 2) ns = 2;
     plan->stages = int32_t(ns);
-    const int64_t ring = ns * stage + kStreamPageWindow * 4;
+    // ring, page-id window, and the per-request table of the slice schedule
+    const int64_t ring = ns * stage + kStreamPageWindow * 4 + kSliceTableInts * 4;
     // Combine slots: four per row set (eight waves on one tile) or two per
     // group (two groups of four waves).
     const int64_t combine = 4 * (int64_t(rt) * ndt * 256 + int64_t(rt) * 32) * 4;
@@ -178,6 +179,25 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
     if (ck > kMaxChunkKeys) ck = kMaxChunkKeys;
   }
   if (ck > int64_t(INT32_MAX) / 2) return VAT_ERR_UNSUPPORTED;
+  // Balanced key slices (streaming kernel, planner's choice, small batches):
+  // one workgroup per CU share of each KV head, whatever the length mix.
+  if (stream && p->chunk_keys == -1 && p->batch <= kSliceMaxBatch) {
+    int64_t nx = int64_t(num_cus) / p->num_kv_heads;
+    if (nx < 1) nx = 1;
+    plan->slices = int32_t(nx);
+    plan->direct = nx == 1 ? 1 : 0;
+    plan->chunk_keys = 0;
+    plan->num_chunk_ids = int32_t(nx + p->batch);  // partial slots: slice + request
+    plan->grid_x = int32_t(nx);
+    plan->grid_y = int32_t(p->num_kv_heads * RB);
+    if (plan->direct) return VAT_OK;
+    const int64_t row_groups = cdiv(M, kMergeRows);
+    plan->merge_grid = int32_t(base_items * row_groups);
+    const int64_t parts = (nx + p->batch) * p->num_kv_heads * RB;
+    const int64_t lse_off = cdiv(parts * M * D * 4, 256) * 256;
+    plan->workspace_bytes = lse_off + cdiv(parts * M * 4, 256) * 256;
+    return VAT_OK;
+  }
   const bool direct = ck >= total_keys;
   const int64_t ids = total_keys / ck + p->batch;
   if (ids > int64_t(INT32_MAX)) return VAT_ERR_UNSUPPORTED;

@@ -30,6 +30,14 @@ constexpr int kMergeThreads = 256;
 constexpr int kChunkQuantum = 16;
 constexpr int kMinChunkKeys = 128;
 constexpr int kMaxChunkKeys = 2048;
+// Batches up to this size are scheduled as balanced key slices (one wave
+// scans the requests' lengths).
+constexpr int kSliceMaxBatch = 64;
+// Request key ranges are padded to this many keys in the slice layout.
+constexpr int kSliceAlign = 16;
+// LDS table of the slice schedule: eight int fields per request.
+constexpr int kSliceTableInts = 8 * kSliceMaxBatch;
+static_assert(kSliceMaxBatch == 64, "one request per lane of a wave64");
 // Largest draft count per request a bit-packed mask may carry (one 64-bit
 // register holds a row).
 constexpr int kMaxMaskedLen = 64;
@@ -55,6 +63,7 @@ struct PartialArgs {
   int32_t page_shift, num_pages, num_kv_indices, num_mask_bytes;
   int32_t rows_per_block, row_blocks, waves_rows, waves_keys;
   int32_t chunk_keys, num_ids, has_mask;
+  int32_t slices;  // > 0: balanced key slices per KV head (streaming kernel, B <= 64)
 };
 
 // Arguments of the merge kernel.
@@ -70,6 +79,7 @@ struct MergeArgs {
   int32_t batch, hq, hkv, group, tokens;
   int32_t page_shift, num_kv_indices;
   int32_t rows_per_block, row_blocks, chunk_keys, num_ids, row_groups;
+  int32_t slices;  // > 0: partials come from balanced key slices, slot = slice + request
 };
 
 // Shape validation (host-detectable errors only).

@@ -336,38 +336,26 @@ __device__ __forceinline__ void combine_waves(StreamAcc<D, RT>& acc, float* slot
 }
 
 // ---------------------------------------------------------------------------
+// One segment of work: keys [lo, hi) of request b for KV head h, all of its
+// query rows. `final_write`: the segment is the whole request, so out and lse
+// are written; otherwise partial slot `slot` is.
 // RT: 16-row tiles per wave. ALT: one row tile, the two wave groups take
 // alternate stages; otherwise group g holds row tiles [g RT, g RT + RT).
 template <int KV, int D, int RT, int NS, bool ALT>
-__global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
+__device__ __forceinline__ void process_segment(const PartialArgs& a, const Req& r, int lo, int hi,
+                                                bool final_write, int slot, int h,
+                                                unsigned char* smem, int wave, int lane) {
   using G = StreamGeom<KV, D>;
-  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int grp = wave / kGroupWaves;
   const int kw = wave % kGroupWaves;
   const int l16 = lane & 15;
   const int j4 = lane >> 4;
-  const int cid = blockIdx.x;
-  const int h = blockIdx.y;
-
-  // ---- work item: chunk `cid` of some request
-  ReqArrays ra{a.kv_indptr, a.last_page_len, a.qo_indptr, a.has_mask ? a.mask_indptr : nullptr,
-               a.batch, a.page_shift, a.chunk_keys, a.num_kv_indices, a.tokens};
-  Req r;
-  Item it;
-  if (!find_item(ra, cid, lane, r, it)) return;
-  const int n_items = chunk_count(r.kv_len, a.chunk_keys);
-  const int j = it.j;
   const int R = a.group * r.L;
-  if (R == 0) return;
-  const int lo = j * a.chunk_keys;
-  const int hi = min(lo + a.chunk_keys, r.kv_len);
   Vis vis{hi, r.prefix, a.has_mask};
   const int last = max(hi - 1, 0);
   const int nst = hi > lo ? (hi - lo + kStageKeys - 1) / kStageKeys : 0;
 
-  // ---- page ids of the chunk into LDS (loads in flight with Q's below)
+  // ---- page ids of the segment into LDS (loads in flight with Q's below)
   int* win = (int*)(smem + NS * G::STAGE);
   const int last_page = last >> a.page_shift;
   int win_base = lo >> a.page_shift;
@@ -421,14 +409,16 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   // Iteration s: wait for this wave's stage-s loads, barrier (everyone's
   // stage-s loads have landed and every wave is done with stage s - 1),
   // refill the buffer of stage s - 1 with stage s + NS - 1, compute stage s.
+  // The barrier after the page-window fill also keeps a previous segment's
+  // combine slots (which alias the stage buffers) safe from the new loads.
+  __syncthreads();
   if (nst > 0) {
     const bool uniform_pages = (1 << a.page_shift) >= G::KPI;
-    __syncthreads();  // page window ready
     auto issue = [&](int s) {
       const int n0 = lo + s * kStageKeys;
       const int p_hi = min(n0 + kStageKeys - 1, last) >> a.page_shift;
       if (p_hi - win_base >= kStreamPageWindow) {
-        // Long chunk: move the window (drains the ring; once per window).
+        // Long segment: move the window (drains the ring; once per window).
         wait_vmcnt<0>();
         __syncthreads();
         win_base = min(n0, last) >> a.page_shift;
@@ -458,12 +448,11 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   else combine_waves<D, RT>(acc, slots, grp, kw, kGroupWaves, lane);
   if (ALT ? wave != 0 : (kw != 0 || !has_rows)) return;
 
-  // ---- write: the request's only chunk -> out (q dtype) and natural-log lse;
+  // ---- write: out (q dtype) and natural-log lse for a whole request;
   // otherwise a normalised fp32 partial (v_scale not yet applied) and its
   // base-2 log-sum-exp.
   constexpr int NDT = D / 16;
-  const bool final_write = n_items == 1;
-  const long long pid = (long long)it.slot * a.hkv + h;
+  const long long pid = (long long)slot * a.hkv + h;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     if (!row_ok[rt]) continue;
@@ -487,6 +476,77 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
       for (int dt = 0; dt < NDT; ++dt) *(f32x4*)(op + 16 * dt + 4 * j4) = acc.o[rt][dt] * inv;
       if (j4 == 0) a.part_lse[pid * a.rows_per_block + local] = lse2;
     }
+  }
+}
+
+template <int KV, int D, int RT, int NS, bool ALT>
+__global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h = blockIdx.y;
+  ReqArrays ra{a.kv_indptr, a.last_page_len, a.qo_indptr, a.has_mask ? a.mask_indptr : nullptr,
+               a.batch, a.page_shift, a.chunk_keys, a.num_kv_indices, a.tokens};
+  Req r;
+  int lo, hi, slot;
+  bool whole;
+  if (a.slices == 0) {
+    // Chunks: work item blockIdx.x is chunk j of some request.
+    Item it;
+    if (!find_item(ra, blockIdx.x, lane, r, it) || r.L == 0) return;
+    lo = it.j * a.chunk_keys;
+    hi = min(lo + a.chunk_keys, r.kv_len);
+    whole = chunk_count(r.kv_len, a.chunk_keys) == 1;
+    slot = it.slot;
+    process_segment<KV, D, RT, NS, ALT>(a, r, lo, hi, whole, slot, h, smem, wave, lane);
+    return;
+  }
+  // Balanced slices: workgroup x takes [x per, (x + 1) per) of the
+  // concatenated key range, request segment by request segment. Every wave
+  // scans the lengths; wave 0 leaves the table in LDS (past the page window)
+  // so nothing per-request stays in registers across segments (field k of
+  // request i at tab[64 k + i]).
+  int* tab = (int*)(smem + NS * StreamGeom<KV, D>::STAGE + kStreamPageWindow * 4);
+  int b, x0, x1;
+  {
+    SliceLanes sl;
+    slice_lanes(ra, a.slices, lane, sl);
+    x0 = blockIdx.x * sl.per;
+    x1 = min(x0 + sl.per, sl.total);
+    b = __popcll(__ballot(lane < a.batch && sl.cum + sl.n <= x0));
+    if (wave == 0) {
+      tab[0 * 64 + lane] = sl.ip0;
+      tab[1 * 64 + lane] = sl.ip1;
+      tab[2 * 64 + lane] = sl.lp;
+      tab[3 * 64 + lane] = sl.q0;
+      tab[4 * 64 + lane] = sl.q1;
+      tab[5 * 64 + lane] = sl.mo;
+      tab[6 * 64 + lane] = sl.cum;
+      tab[7 * 64 + lane] = sl.n;
+    }
+  }
+  if (x0 >= x1) return;
+  __syncthreads();
+  for (; b < a.batch; ++b) {
+    const int cb = __builtin_amdgcn_readfirstlane(tab[6 * 64 + b]);
+    if (cb >= x1) break;
+    if (__builtin_amdgcn_readfirstlane(tab[7 * 64 + b]) == 0) continue;
+    r = make_req(__builtin_amdgcn_readfirstlane(tab[b]), __builtin_amdgcn_readfirstlane(tab[64 + b]),
+                 __builtin_amdgcn_readfirstlane(tab[128 + b]),
+                 __builtin_amdgcn_readfirstlane(tab[192 + b]),
+                 __builtin_amdgcn_readfirstlane(tab[256 + b]),
+                 __builtin_amdgcn_readfirstlane(tab[320 + b]), a.page_shift, a.num_kv_indices,
+                 a.tokens);
+    lo = max(x0 - cb, 0);
+    hi = min(x1 - cb, r.kv_len);
+    if (lo >= hi) continue;
+    // Opaque copies of the lane coordinates: what the segment derives from
+    // them is recomputed per segment instead of being hoisted out of this
+    // loop and held in registers across it.
+    int lane_s = lane, wave_s = wave, h_s = h;
+    asm volatile("" : "+v"(lane_s), "+v"(wave_s), "+s"(h_s));
+    process_segment<KV, D, RT, NS, ALT>(a, r, lo, hi, lo == 0 && hi == r.kv_len, blockIdx.x + b, h_s,
+                                        smem, wave_s, lane_s);
   }
 }
 

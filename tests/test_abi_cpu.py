@@ -1,0 +1,297 @@
+"""The C ABI without a GPU: symbols, host validation and the shape-only planner.
+
+Every call here fails (or plans) before anything reaches the HIP runtime, so
+the library is loaded and exercised on a machine with no GPU. Problems pass
+num_cus > 0 so the planner never queries a device.
+"""
+
+import ctypes
+import math
+import os
+import re
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+from paged_kv_gqa_planner_amd import binding as B
+from workloads import make_config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "verify_attention.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libvat.so not built (run __graft_entry__.build())")
+    return B.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:vat_status_t|const char\*|int32_t)\s+(\w+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_library_exports_every_header_function(lib):
+    names = header_functions()
+    assert {"verify_attention", "vat_plan", "vat_workspace_size", "vat_launch_partial",
+            "vat_launch_merge", "vat_status_string", "vat_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.vat_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert lib.vat_status_string(code).decode()
+    assert lib.vat_status_string(99).decode() == "unknown status"
+
+
+def problem_of(p, **kw):
+    fields = dict(batch=p.batch, num_qo_heads=p.num_qo_heads, num_kv_heads=p.num_kv_heads,
+                  head_dim=p.head_dim, page_size=p.page_size, num_pages=p.num_pages,
+                  num_kv_indices=len(p.kv_indices), num_qo_tokens=p.num_tokens,
+                  max_qo_len=p.max_qo_len, q_dtype={"f32": 0, "bf16": 1}[p.q_dtype],
+                  kv_dtype={"f32": 0, "bf16": 1, "e4m3": 2}[p.kv_dtype],
+                  has_mask=p.mask is not None,
+                  num_mask_bytes=0 if p.mask is None else len(p.mask), num_cus=256)
+    fields.update(kw)
+    return B.make_problem(**fields)
+
+
+def base_problem(**kw):
+    f = dict(batch=2, num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=16, num_pages=64,
+             num_kv_indices=40, num_qo_tokens=10, max_qo_len=5, q_dtype=1, kv_dtype=1, has_mask=0,
+             num_mask_bytes=0, num_cus=256, chunk_keys=-1)
+    f.update(kw)
+    return B.make_problem(**f)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+def test_plans_for_the_workloads(lib, cid):
+    p = make_config(cid, prefix=32768 if cid == 3 else 4096)
+    plan = B.vat_plan(problem_of(p))
+    G = p.num_qo_heads // p.num_kv_heads
+    assert plan.group == G and plan.rows == G * p.max_qo_len
+    assert plan.rows_per_block * plan.row_blocks >= plan.rows
+    assert plan.grid_y == p.num_kv_heads * plan.row_blocks
+    if plan.slices:
+        # Balanced slices: one workgroup per (slice, KV head), CU-filling.
+        assert plan.kernel == 1 and plan.chunk_keys == 0
+        assert plan.slices == max(1, 256 // p.num_kv_heads) == plan.grid_x
+        assert plan.num_chunk_ids == plan.slices + p.batch
+    else:
+        assert plan.chunk_keys % 16 == 0 and plan.chunk_keys > 0
+        total_keys = len(p.kv_indices) * p.page_size
+        assert plan.num_chunk_ids == total_keys // plan.chunk_keys + p.batch
+    assert plan.lds_bytes <= 160 * 1024
+    if cid == 1:
+        assert plan.kernel == 0 and plan.slices == 0  # fp32 caches take the row-tiled kernel
+    elif cid == 4:
+        assert plan.kernel == 0 and plan.direct == 1 and plan.workspace_bytes == 0
+    else:
+        assert plan.kernel == 1 and plan.threads == 512 and plan.slices > 0
+    if not plan.direct:
+        parts = plan.num_chunk_ids * p.num_kv_heads * plan.row_blocks
+        assert plan.workspace_bytes >= parts * plan.rows_per_block * (p.head_dim + 1) * 4
+        assert plan.merge_grid > 0
+
+
+def test_plan_is_shape_only_and_deterministic(lib):
+    a = B.vat_plan(base_problem()).as_dict()
+    b = B.vat_plan(base_problem()).as_dict()
+    assert a == b
+    # Doubling the CU count never shortens the chunk the planner picks.
+    c = B.vat_plan(base_problem(num_kv_indices=4000, num_cus=512)).as_dict()
+    d = B.vat_plan(base_problem(num_kv_indices=4000, num_cus=256)).as_dict()
+    assert c["chunk_keys"] <= d["chunk_keys"]
+
+
+def test_forced_chunk_and_direct(lib):
+    assert B.vat_plan(base_problem(chunk_keys=0)).direct == 1
+    p = B.vat_plan(base_problem(chunk_keys=48))
+    assert p.chunk_keys == 48 and p.direct == 0
+    assert B.vat_workspace_size(base_problem(chunk_keys=0)) == 0
+    assert B.vat_workspace_size(base_problem(chunk_keys=48)) == p.workspace_bytes > 0
+
+
+def test_chunk_ids_of_consecutive_requests_are_disjoint():
+    # Host-side check of the id layout the kernels use: request b's chunks are
+    # start_b .. start_b + ceil(kv_len_b / C) - 1 with
+    # start_b = floor(kv_indptr[b] * page_size / C) + b.
+    rng = np.random.default_rng(0)
+    for _ in range(300):
+        ps = int(rng.choice([1, 4, 16, 64]))
+        C = int(rng.choice([16, 48, 64, 528, 2048]))
+        pages = rng.integers(0, 40, size=int(rng.integers(1, 20)))
+        indptr = np.concatenate([[0], np.cumsum(pages)])
+        cap = int(indptr[-1]) + int(rng.integers(0, 5))
+        used = set()
+        for b in range(len(pages)):
+            kv_len = 0 if pages[b] == 0 else (pages[b] - 1) * ps + int(rng.integers(1, ps + 1))
+            start = (int(indptr[b]) * ps) // C + b
+            for j in range(math.ceil(kv_len / C)):
+                cid = start + j
+                assert cid not in used and cid < (cap * ps) // C + len(pages)
+                used.add(cid)
+
+
+def slice_segments(kv_lens, qo_lens, slices, align=16):
+    """Host restatement of the balanced-slice layout: the (slice, request, lo,
+    hi, slot) segments the streaming kernel processes, and per request the
+    slots the merge reads (x_lo .. x_hi, slot x + b)."""
+    n = [(-(-k // align) * align) if (q > 0 and k > 0) else 0 for k, q in zip(kv_lens, qo_lens)]
+    cum = np.concatenate([[0], np.cumsum(n)]).astype(int)
+    total = int(cum[-1])
+    per = -(-(-(-total // slices)) // align) * align if total else 0
+    segs = []
+    for x in range(slices):
+        x0, x1 = x * per, min((x + 1) * per, total)
+        if x0 >= x1:
+            continue
+        for b in range(len(n)):
+            if cum[b] >= x1 or n[b] == 0:
+                continue
+            lo, hi = max(x0 - cum[b], 0), min(x1 - cum[b], kv_lens[b])
+            if lo < hi:
+                segs.append((x, b, lo, hi, x + b))
+    merged = {}
+    for b in range(len(n)):
+        if n[b]:
+            x_lo, x_hi = cum[b] // per, (cum[b] + kv_lens[b] - 1) // per
+            merged[b] = [x + b for x in range(x_lo, x_hi + 1)]
+    return segs, merged
+
+
+def test_slice_segments_cover_each_request_once():
+    rng = np.random.default_rng(1)
+    for _ in range(400):
+        B = int(rng.integers(1, 65))
+        kv = rng.integers(0, 3000, size=B)
+        kv[rng.random(B) < 0.1] = 0
+        q = np.minimum(rng.integers(0, 9, size=B), kv)
+        slices = int(rng.integers(1, 300))
+        segs, merged = slice_segments(list(kv), list(q), slices)
+        slots = [s[4] for s in segs]
+        assert len(set(slots)) == len(slots) and all(s < slices + B for s in slots)
+        for b in range(B):
+            mine = sorted((lo, hi, slot) for (_, bb, lo, hi, slot) in segs if bb == b)
+            if q[b] == 0 or kv[b] == 0:
+                assert not mine
+                continue
+            assert mine[0][0] == 0 and mine[-1][1] == kv[b]
+            assert all(mine[i][1] == mine[i + 1][0] for i in range(len(mine) - 1))
+            whole = len(mine) == 1
+            # The merge reads exactly the slots written as partials.
+            assert (merged[b] == [m[2] for m in mine]) or (whole and len(merged[b]) == 1)
+            assert all(lo % 16 == 0 for lo, _, _ in mine)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_qo_heads=6, num_kv_heads=4), 2),
+    (dict(head_dim=96), 3),
+    (dict(page_size=12), 3),
+    (dict(page_size=512), 3),
+    (dict(q_dtype=0, kv_dtype=1), 3),
+    (dict(q_dtype=1, kv_dtype=0), 3),
+    (dict(has_mask=1, max_qo_len=65, num_mask_bytes=600), 3),
+    (dict(chunk_keys=40), 2),
+    (dict(chunk_keys=-2), 2),
+    (dict(batch=-1), 2),
+    (dict(num_pages=0), 2),
+])
+def test_invalid_problems_are_rejected_on_the_host(lib, kw, code):
+    plan = B.VatPlan()
+    assert lib.vat_plan(ctypes.byref(base_problem(**kw)), ctypes.byref(plan)) == code
+
+
+def _call(lib, prob, ptrs=None, scales=(0.1, 1.0, 1.0), ws=0, ws_bytes=0):
+    fake = 0x10000
+    p = dict(q=fake, k=fake, v=fake, indptr=fake, indices=fake, lpl=fake, qo=fake, mask=0,
+             mask_indptr=0, out=fake, lse=fake)
+    if ptrs:
+        p.update(ptrs)
+    return lib.verify_attention(ctypes.byref(prob), p["q"], p["k"], p["v"], p["indptr"],
+                                p["indices"], p["lpl"], p["qo"], p["mask"], p["mask_indptr"],
+                                scales[0], scales[1], scales[2], p["out"], p["lse"], ws, ws_bytes,
+                                None)
+
+
+def test_host_checks_before_any_launch(lib):
+    prob = base_problem(chunk_keys=0)  # direct: no workspace
+    assert _call(lib, prob, ptrs=dict(q=0)) == 1
+    assert _call(lib, prob, ptrs=dict(lse=0)) == 1
+    assert _call(lib, prob, ptrs=dict(q=0x10002)) == 4
+    assert _call(lib, prob, ptrs=dict(out=0x10008)) == 4
+    assert _call(lib, prob, scales=(0.0, 1.0, 1.0)) == 2
+    assert _call(lib, prob, scales=(float("nan"), 1.0, 1.0)) == 2
+    assert _call(lib, prob, scales=(0.1, -1.0, 1.0)) == 2
+    assert _call(lib, prob, scales=(0.1, 1.0, float("inf"))) == 2
+    masked = base_problem(chunk_keys=0, has_mask=1, num_mask_bytes=8)
+    assert _call(lib, masked, ptrs=dict(mask=0x20000, mask_indptr=0)) == 1
+    split = base_problem(chunk_keys=48)
+    need = B.vat_workspace_size(split)
+    assert _call(lib, split, ws=0, ws_bytes=0) == 1
+    assert _call(lib, split, ws=0x40000, ws_bytes=need - 1) == 5
+    assert _call(lib, split, ws=0x40010, ws_bytes=need) == 4
+
+
+def test_empty_work_returns_ok_without_a_gpu(lib):
+    assert _call(lib, base_problem(num_qo_tokens=0), ptrs=dict(q=0, out=0, lse=0)) == 0
+    assert _call(lib, base_problem(batch=0, num_qo_tokens=0)) == 0
+    assert _call(lib, base_problem(max_qo_len=0)) == 0
+
+
+def test_planner_under_address_and_ub_sanitizers(tmp_path):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    driver = tmp_path / "plan_fuzz.cpp"
+    driver.write_text(r'''
+#include <stdio.h>
+#include <stdlib.h>
+#include "plan.h"
+int main() {
+  srand(7);
+  const int dims[] = {32, 64, 96, 128}, pss[] = {1, 2, 16, 12, 256, 512};
+  long ok = 0;
+  for (int it = 0; it < 200000; ++it) {
+    vat_problem_t p;
+    p.batch = rand() % 300 - 2;
+    p.num_kv_heads = 1 + rand() % 16;
+    p.num_qo_heads = p.num_kv_heads * (1 + rand() % 16) + (rand() % 10 == 0);
+    p.head_dim = dims[rand() % 4];
+    p.page_size = pss[rand() % 6];
+    p.num_pages = rand() % 100000;
+    p.num_kv_indices = rand() % 2000000;
+    p.num_qo_tokens = rand() % 100000;
+    p.max_qo_len = rand() % 2000;
+    p.q_dtype = rand() % 3; p.kv_dtype = rand() % 3;
+    p.has_mask = rand() % 3;
+    p.num_mask_bytes = rand() % 100000;
+    p.num_cus = 1 + rand() % 512;
+    p.chunk_keys = (rand() % 4 == 0) ? (rand() % 3) * 16 - 16 : -1;
+    vat_plan_t plan;
+    if (vat::make_plan(&p, p.num_cus, &plan) == VAT_OK) {
+      ++ok;
+      if (plan.lds_bytes > 160 * 1024 || plan.workspace_bytes < 0) { printf("bad plan\n"); return 1; }
+    }
+  }
+  printf("planned %ld\n", ok);
+  return ok > 0 ? 0 : 1;
+}
+''')
+    exe = tmp_path / "plan_fuzz"
+    csrc = os.path.join(ROOT, "paged_kv_gqa_planner_amd", "csrc")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-I", csrc, "-I", os.path.join(ROOT, "include"),
+           str(driver), os.path.join(csrc, "plan.cpp"), "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "planned" in r.stdout

@@ -187,6 +187,46 @@ def test_any_split_matches_oracle(gpu_lib, chunk):
     compare(p, *to_f64(out, lse), *oracle_of(p), what=f"chunk {chunk}")
 
 
+# ---------------------------------------------------------------- balanced slices
+
+
+SLICE_CASES = {
+    # mixed lengths (and requests without drafts) over many slices
+    "mixed_bf16": dict(prefix_lens=[3000, 0, 17, 900, 5000, 64, 1, 2500], qo_lens=[4, 2, 0, 8, 1, 3, 5, 6],
+                       num_qo_heads=32, num_kv_heads=8, head_dim=128, mask_kind="tree"),
+    "mixed_e4m3": dict(prefix_lens=[700, 4100, 33, 2222], qo_lens=[8, 1, 5, 3], num_qo_heads=16,
+                       num_kv_heads=2, head_dim=128, kv_dtype="e4m3", fp8_absmax_scales=True,
+                       mask_kind="causal"),
+    "d64_ps4": dict(prefix_lens=[1000, 250, 3100], qo_lens=[2, 7, 4], num_qo_heads=8, num_kv_heads=4,
+                    head_dim=64, page_size=4, mask_kind="random", mask_density=0.5),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SLICE_CASES))
+@pytest.mark.parametrize("num_cus", [1, 8, 40, 256, 2048])
+def test_balanced_slices_match_oracle(gpu_lib, name, num_cus):
+    # The slice count follows the CU count the plan is made for, so these cover
+    # one slice (direct), a few long slices spanning several requests, and more
+    # slices than keys (empty slices).
+    p = make_case(91, **SLICE_CASES[name])
+    plan = gpu_lib.vat_plan(_problem(gpu_lib, p, num_cus=num_cus))
+    say(f"[slices {name} num_cus={num_cus}] slices={plan.slices} direct={plan.direct}")
+    assert plan.slices >= 1
+    out, lse = run_gpu(gpu_lib, p, num_cus=num_cus)
+    compare(p, *to_f64(out, lse), *oracle_of(p), what=f"{name} cus {num_cus}")
+
+
+def test_long_request_moves_the_page_window(gpu_lib):
+    # One request longer than the in-LDS page window (2048 pages of 16 keys)
+    # processed whole by one workgroup.
+    p = make_case(92, prefix_lens=[36000], qo_lens=[5], num_qo_heads=8, num_kv_heads=1,
+                  head_dim=128, mask_kind="tree")
+    for num_cus, chunk in ((1, -1), (256, 0)):
+        say(f"[long request num_cus={num_cus} chunk={chunk}]")
+        out, lse = run_gpu(gpu_lib, p, num_cus=num_cus, chunk_keys=chunk)
+        compare(p, *to_f64(out, lse), *oracle_of(p), what="long request")
+
+
 # ---------------------------------------------------------------- graph capture
 
 
