@@ -27,6 +27,28 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? l
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Transposing LDS read (ds_read_b64_tr_b16) written as inline asm. The
+// compiler cannot tell which LDS bytes the still-running DMA loads of later
+// stages will write, so for the builtin form it waits for every outstanding
+// vector memory load (vmcnt(0)) first, which serialises the stage ring. The
+// caller orders this read after its own wait for the stage and must call
+// lds_wait_tied before using the result.
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
+  s16x4 v;
+  const unsigned addr = (unsigned)(uintptr_t)(const lds_void_t*)p;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+
+// Wait until at most N LDS/scalar-memory operations are outstanding (LDS
+// operations complete in order, so the reads issued before the last N have
+// landed) and tie the wait to `v`, so its consumers cannot be scheduled above.
+template <int N>
+__device__ __forceinline__ void lds_wait_tied(s16x4& v) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
+}
+
 // Max / sum over the four lanes l, l^16, l^32, l^48 that hold one query row.
 __device__ __forceinline__ float row_max4(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));

@@ -25,6 +25,8 @@
 // The waves' partial results are combined through LDS; a chunk that is its
 // request's only one writes out and lse, otherwise a normalised fp32 partial
 // and its base-2 log-sum-exp go to the workspace for the merge.
+#include <utility>
+
 #include "device_common.h"
 
 namespace vat {
@@ -259,10 +261,10 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
     pb[rt] = __builtin_bit_cast(s16x4, u32x2{cvt_pk_bf16(st[rt][0], st[rt][1]),
                                              cvt_pk_bf16(st[rt][2], st[rt][3])});
   const unsigned char* vb = stage + G::BLK;
+  constexpr int NDT = D / 16;
+  if constexpr (KV == KV_E4M3) {
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    s16x4 va;
-    if constexpr (KV == KV_E4M3) {
+    for (int dt = 0; dt < NDT; ++dt) {
       // Lane (d = l % 16, j = l / 16): codes of keys 16 kw + 4 j + e at d.
       const int kl0 = 16 * kw + 4 * j4;
       const int byte = 16 * dt + l16;
@@ -272,21 +274,34 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
       for (int e = 0; e < 4; ++e)
         b[e] = vb[(kl0 + e) * G::ROW + (swz<G::CPK>(kl0 + e, ch) << 4) + within];
       const unsigned packed = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-      va = __builtin_bit_cast(s16x4, u32x2{e4m3x2_to_bf16x2(packed, false), e4m3x2_to_bf16x2(packed, true)});
-    } else {
-      // Transpose load: source lane s of each 16-lane group points at the
-      // 8 bytes V[key 16 kw + 4 j + s / 4][d = 16 dt + 4 (s % 4) ..]; lane
-      // (d, j) then receives V[16 kw + 4 j + e][16 dt + d], e = 0..3.
-      const int kl = 16 * kw + 4 * j4 + (l16 >> 2);
+      const s16x4 va = __builtin_bit_cast(
+          s16x4, u32x2{e4m3x2_to_bf16x2(packed, false), e4m3x2_to_bf16x2(packed, true)});
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        acc.o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[rt], acc.o[rt][dt], 0, 0, 0);
+    }
+  } else {
+    // Transpose loads: source lane s of each 16-lane group points at the 8
+    // bytes V[key 16 kw + 4 j + s / 4][d = 16 dt + 4 (s % 4) ..]; lane (d, j)
+    // then receives V[16 kw + 4 j + e][16 dt + d], e = 0..3. All NDT reads
+    // are issued first; tile dt waits only for its own.
+    const int kl = 16 * kw + 4 * j4 + (l16 >> 2);
+    s16x4 va[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
       const int d0 = 16 * dt + 4 * (l16 & 3);
       const int ch = d0 >> 3;
-      const int off = kl * G::ROW + (swz<G::CPK>(kl, ch) << 4) + (d0 & 7) * 2;
-      va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(lds_void_t*)(vb + off));
+      va[dt] = lds_read_tr16(vb + kl * G::ROW + (swz<G::CPK>(kl, ch) << 4) + (d0 & 7) * 2);
     }
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      ((lds_wait_tied<NDT - 1 - I>(va[I]),
+        [&] {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-      acc.o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[rt], acc.o[rt][dt], 0, 0, 0);
+          for (int rt = 0; rt < RT; ++rt)
+            acc.o[rt][I] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[I], pb[rt], acc.o[rt][I], 0, 0, 0);
+        }()),
+       ...);
+    }(std::make_integer_sequence<int, NDT>{});
   }
 }
 
@@ -355,12 +370,6 @@ __device__ __forceinline__ void process_segment(const PartialArgs& a, const Req&
   const int last = max(hi - 1, 0);
   const int nst = hi > lo ? (hi - lo + kStageKeys - 1) / kStageKeys : 0;
 
-  // ---- page ids of the segment into LDS (loads in flight with Q's below)
-  int* win = (int*)(smem + NS * G::STAGE);
-  const int last_page = last >> a.page_shift;
-  int win_base = lo >> a.page_shift;
-  if (nst > 0) fill_page_window(win, a, r, win_base, last_page);
-
   // ---- rows: tile rt of this wave, lane row row0 + rt * 16 + l16
   const int row0 = ALT ? 0 : grp * RT * 16;
   int row_t[RT], row_g[RT];
@@ -393,6 +402,16 @@ __device__ __forceinline__ void process_segment(const PartialArgs& a, const Req&
       qf[rt][4 * ks + 3] = x.w;
     }
   }
+  // ---- page ids of the segment into LDS. The Q and mask loads above are in
+  // flight meanwhile; all of them have landed once this returns, so the ring
+  // below starts with no register load outstanding (a load still pending
+  // there would make every stage wait for all of its queued DMA).
+  int* win = (int*)(smem + NS * G::STAGE);
+  const int last_page = last >> a.page_shift;
+  int win_base = lo >> a.page_shift;
+  if (nst > 0) fill_page_window(win, a, r, win_base, last_page);
+  wait_vmcnt<0>();
+
   // A group whose tiles hold no row skips the math (it still issues loads).
   const bool has_rows = row0 < R;
 
