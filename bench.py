@@ -274,7 +274,7 @@ def main():
         entry = tr.get(str(args.config) if args.config != 3 else f"3@{args.prefix}")
         if entry and entry.get("source_hash") == src_hash:
             roof["traffic"] = entry.get("bytes_per_launch")
-    roof["kernel"] = "vat_partial"
+    roof["kernel"] = "vat_stream" if plan["kernel"] == 1 else "vat_tile"
     roof["algorithmic_bytes_per_launch"] = kvb
     roof["algorithmic_flops_per_launch"] = flops
 
