@@ -110,18 +110,24 @@ typedef struct {
 typedef struct {
   int32_t direct;           /* 1: every request fits one chunk: no merge kernel,
                                the partial kernel writes out/lse itself */
-  int32_t kernel;           /* 1: LDS-ring streaming kernel (bf16/fp8 KV, <= 80
-                               query rows per KV head); 0: row-tiled kernel */
+  int32_t kernel;           /* 1: LDS-ring streaming kernel (bf16/fp8 KV, at most
+                               256 (bf16) or 128 (fp8) query rows per KV head);
+                               0: row-tiled kernel */
   int32_t stages;           /* streaming kernel: 64-key stages in flight in LDS */
-  int32_t slices;           /* > 0: balanced scheduling. Per KV head, the requests'
-                               keys (each padded to 16) are laid end to end and cut
-                               into `slices` equal ranges, one workgroup each; 0:
-                               each request is cut into chunk_keys-long chunks */
+  int32_t slices;           /* > 0: balanced scheduling. Per KV head, the page-index
+                               space [0, num_kv_indices) is cut into `slices` equal
+                               ranges, one workgroup each, which processes the
+                               requests' pages inside it; 0: each request is cut
+                               into chunk_keys-long chunks */
   int32_t group;            /* G = Hq / Hkv */
   int32_t rows;             /* G * max_qo_len query rows per (request, KV head) */
   int32_t row_tiles_per_wave; /* 16-row MFMA tiles each wave holds */
   int32_t waves_rows;       /* waves splitting a row block's rows */
-  int32_t waves_keys;       /* waves splitting each key range */
+  int32_t waves_keys;       /* waves splitting each key range (streaming kernel:
+                               waves per row tile set, each taking a share of
+                               every 64-key stage) */
+  int32_t dma_waves;        /* streaming kernel: waves issuing the K/V loads (the
+                               last dma_waves of eight) */
   int32_t rows_per_block;   /* M = waves_rows * row_tiles_per_wave * 16 */
   int32_t row_blocks;       /* RB = ceil(rows / M) */
   int32_t chunk_keys;       /* keys per chunk: request b's keys [0, kv_len_b) form

@@ -33,7 +33,7 @@ class VatProblem(ctypes.Structure):
 
 class VatPlan(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
-        "direct", "kernel", "stages", "slices", "group", "rows", "row_tiles_per_wave", "waves_rows", "waves_keys",
+        "direct", "kernel", "stages", "slices", "group", "rows", "row_tiles_per_wave", "waves_rows", "waves_keys", "dma_waves",
         "rows_per_block", "row_blocks", "chunk_keys", "num_chunk_ids", "grid_x", "grid_y",
         "threads", "lds_bytes", "merge_grid", "merge_threads", "num_cus")] + [
         ("workspace_bytes", ctypes.c_int64)]

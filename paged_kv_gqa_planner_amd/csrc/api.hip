@@ -10,7 +10,7 @@
 
 namespace vat {
 const void* tile_kernel(int kv_dtype, int head_dim, int rt);
-const void* stream_kernel(int kv_dtype, int head_dim, int rt);
+const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int pair);
 const void* merge_kernel(int q_is_f32, int head_dim);
 }  // namespace vat
 
@@ -128,7 +128,8 @@ vat_status_t launch_partial(const vat_problem_t* p, const vat_plan_t& plan, cons
   a.num_ids = plan.num_chunk_ids;
   a.has_mask = p->has_mask;
   a.slices = plan.slices;
-  const void* fn = plan.kernel ? vat::stream_kernel(p->kv_dtype, p->head_dim, plan.rows_per_block / 16)
+  const void* fn = plan.kernel ? vat::stream_kernel(p->kv_dtype, p->head_dim, plan.row_tiles_per_wave, plan.dma_waves,
+                                              plan.waves_keys)
                                : vat::tile_kernel(p->kv_dtype, p->head_dim, plan.row_tiles_per_wave);
   if (plan.lds_bytes > 65536) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, plan.lds_bytes) !=

@@ -48,6 +48,11 @@ __device__ __forceinline__ void lds_wait_tied(s16x4& v) {
   static_assert(N >= 0 && N < 16, "lgkmcnt range");
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
 }
+template <int N>
+__device__ __forceinline__ void lds_wait_tied2(s16x4& v, s16x4& w) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(v), "+v"(w) : "n"(N));
+}
 
 // Max / sum over the four lanes l, l^16, l^32, l^48 that hold one query row.
 __device__ __forceinline__ float row_max4(float x) {
@@ -243,49 +248,6 @@ __device__ __forceinline__ bool find_item(const ReqArrays& ra, int c, int lane, 
   it.j = c - chunk_start(r.kv_start, ra.page_shift, ra.chunk, b);
   it.slot = c;
   return it.j >= 0 && it.j < chunk_count(r.kv_len, ra.chunk) && r.L > 0;
-}
-
-// Balanced key slices (batches of at most 64 requests). Lane i holds request
-// i; its keys, padded to kSliceAlign, occupy [cum_i, cum_i + n_i) of one
-// concatenated key range (requests without query tokens take none), which is
-// cut into `slices` ranges of `per` keys. Slice x holds the part of request b
-// between max(x per - cum_b, 0) and min((x + 1) per - cum_b, kv_len_b).
-struct SliceLanes {
-  int ip0, ip1, lp, q0, q1, mo;  // this lane's request entries
-  int cum, n;                    // its padded key range
-  int total, per;                // wave-uniform
-};
-
-__device__ __forceinline__ void slice_lanes(const ReqArrays& ra, int slices, int lane, SliceLanes& s) {
-  const bool in = lane < ra.batch;
-  const int i = in ? lane : 0;
-  s.ip0 = ra.kv_indptr[i];
-  s.ip1 = ra.kv_indptr[i + 1];
-  s.lp = in ? ra.last_page_len[i] : 1;
-  s.q0 = ra.qo_indptr[i];
-  s.q1 = ra.qo_indptr[i + 1];
-  s.mo = ra.mask_indptr ? ra.mask_indptr[i] : 0;
-  const Req mine = make_req(s.ip0, s.ip1, s.lp, s.q0, s.q1, s.mo, ra.page_shift, ra.num_kv_indices,
-                            ra.tokens);
-  s.n = (in && mine.L > 0) ? (mine.kv_len + kSliceAlign - 1) / kSliceAlign * kSliceAlign : 0;
-  int incl = s.n;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int up = __shfl_up(incl, o);
-    if (lane >= o) incl += up;
-  }
-  s.cum = incl - s.n;
-  s.total = __builtin_amdgcn_readlane(incl, 63);
-  const int per = (s.total + slices - 1) / slices;
-  s.per = (per + kSliceAlign - 1) / kSliceAlign * kSliceAlign;
-}
-
-// Request b's geometry from the lanes (wave-uniform).
-__device__ __forceinline__ Req slice_req(const ReqArrays& ra, const SliceLanes& s, int b) {
-  return make_req(__builtin_amdgcn_readlane(s.ip0, b), __builtin_amdgcn_readlane(s.ip1, b),
-                  __builtin_amdgcn_readlane(s.lp, b), __builtin_amdgcn_readlane(s.q0, b),
-                  __builtin_amdgcn_readlane(s.q1, b), __builtin_amdgcn_readlane(s.mo, b),
-                  ra.page_shift, ra.num_kv_indices, ra.tokens);
 }
 
 // Bits j = 0..L-1 of row t of the request's packed L x L mask block.

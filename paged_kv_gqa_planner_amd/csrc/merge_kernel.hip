@@ -5,8 +5,8 @@
 //
 // One wave per query row (each lane owns D / 64 head dims), four rows per
 // workgroup, partials combined online eight at a time. A request's partials
-// are its chunks (ids from chunk_start) or, with balanced slices, the slices
-// x_lo .. x_hi its keys fall in (slot x + b). Requests that fit one chunk or
+// are its chunks (ids from chunk_start) or, with balanced slices of the
+// page-index space, the slices x_lo .. x_hi its pages fall in (slot x + b). Requests that fit one chunk or
 // slice were written directly by the partial kernel and are skipped.
 #include "device_common.h"
 
@@ -24,18 +24,17 @@ __global__ __launch_bounds__(kMergeThreads) void vat_merge(MergeArgs a) {
   x /= a.row_blocks;
   const int h = x % a.hkv;
   const int b = x / a.hkv;
-  ReqArrays ra{a.kv_indptr, a.last_page_len, a.qo_indptr, nullptr, a.batch, a.page_shift,
-               a.chunk_keys, a.num_kv_indices, a.tokens};
   Req r;
   int n, first;  // partials of request b: slots first + i, i < n
   if (a.slices > 0) {
-    SliceLanes sl;
-    slice_lanes(ra, a.slices, lane, sl);
-    r = slice_req(ra, sl, b);
-    if (r.L == 0 || r.kv_len == 0) return;
-    const int cb = __builtin_amdgcn_readlane(sl.cum, b);
-    const int x_lo = cb / sl.per;
-    const int x_hi = (cb + r.kv_len - 1) / sl.per;
+    // Slices of the page-index space, `per` pages each: request b's pages
+    // [kv_indptr[b], kv_indptr[b + 1]) fall in slices x_lo .. x_hi.
+    r = make_req(a.kv_indptr[b], a.kv_indptr[b + 1], a.last_page_len[b], a.qo_indptr[b],
+                 a.qo_indptr[b + 1], 0, a.page_shift, a.num_kv_indices, a.tokens);
+    if (r.L == 0 || r.pages == 0) return;
+    const int per = (a.num_kv_indices + a.slices - 1) / a.slices;
+    const int x_lo = r.kv_start / per;
+    const int x_hi = (r.kv_start + r.pages - 1) / per;
     n = x_hi - x_lo + 1;
     first = x_lo + b;
   } else {

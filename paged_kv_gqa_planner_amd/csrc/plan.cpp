@@ -73,23 +73,31 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   const int64_t eb = elem_bytes(p->kv_dtype);
 
   // Kernel and row tiling.
-  //  * Streaming kernel (bf16 / fp8 caches, at most six 16-row tiles per KV
-  //    head -- every verify shape): one row block; each group of four waves
-  //    splits a 64-key stage into 16-key tiles, and the two groups split the
-  //    row tiles (or alternate stages when there is one tile), so each key is
-  //    read from HBM once and from LDS once or twice.
+  //  * Streaming kernel (bf16 / fp8 caches, at most sixteen 16-row tiles per
+  //    KV head -- every verify shape): one row block; wave w of eight computes
+  //    row tiles [w rt, w rt + rt) over all keys (rt = 1 up to eight tiles,
+  //    else 2), so each key is read from HBM once and no two waves share a
+  //    row's softmax state.
   //  * Row-tiled kernel (fp32 caches, wider row sets such as prefill): a wave
   //    holds RT tiles; waves split the rows and, when rows are few, the keys.
   int rt, wr, wk;
-  // fp8 caches with D = 64 have too few 1 KB loads per stage for eight waves.
-  const bool stream = (p->kv_dtype != VAT_F32) && tiles <= kStreamMaxTiles &&
-                      !(p->kv_dtype == VAT_FP8_E4M3FN && p->head_dim == 64);
+  // fp8 caches with D = 64 have too few 1 KB loads per stage for eight waves;
+  // with fp8 the decode registers leave room for one row tile per wave.
+  const bool fp8 = p->kv_dtype == VAT_FP8_E4M3FN;
+  const bool stream = (p->kv_dtype != VAT_F32) &&
+                      tiles <= (fp8 ? kStreamThreads / 64 : kStreamMaxTiles) &&
+                      !(fp8 && p->head_dim == 64);
+  int dw = 0;
   if (stream) {
-    // One row tile: both wave groups hold it and take alternate stages.
-    // Otherwise the two groups split ceil(tiles / 2) tiles each.
-    rt = tiles == 1 ? 1 : int(cdiv(tiles, 2));
-    wr = tiles == 1 ? 1 : 2;
-    wk = tiles == 1 ? 2 * kWaves : kWaves;
+    rt = tiles <= kStreamThreads / 64 ? 1 : 2;
+    wr = int(cdiv(tiles, rt));
+    // One or two row tiles: two waves per tile split every stage's keys
+    // (their softmax states meet in LDS at the end of each segment), so four
+    // SIMDs share the math.
+    wk = tiles <= 2 ? 2 : 1;
+    // Up to four computing waves leave the last four to issue the DMA alone,
+    // so a computing wave never stalls behind the memory queue.
+    dw = wr * wk <= 4 ? 4 : kStreamThreads / 64;
   } else if (tiles <= 3) {
     rt = int(tiles);
     wr = 1;
@@ -114,13 +122,13 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   plan->row_tiles_per_wave = rt;
   plan->waves_rows = wr;
   plan->waves_keys = wk;
+  plan->dma_waves = dw;
   plan->rows_per_block = int32_t(M);
   plan->row_blocks = int32_t(RB);
   if (int64_t(p->num_kv_heads) * RB > 65535) return VAT_ERR_UNSUPPORTED;
 
   // LDS. Streaming: a ring of 64-key stages (K and V), as many as fit the
-  // budget (2..8), plus the segment's page ids and the slice table; the
-  // waves' final combine reuses the ring. Row-tiled: a
+  // budget (2..8), plus the work item's page ids. Row-tiled: a
   // per-wave 32-key V staging tile (bf16 after any fp8 decode) and the slots
   // of the key-splitting waves' combine.
   const int64_t ndt = D / 16;
@@ -130,12 +138,9 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
     if (ns > 8) ns = 8;
     if (ns < 2) ns = 2;
     plan->stages = int32_t(ns);
-    // ring, page-id window, and the per-request table of the slice schedule
-    const int64_t ring = ns * stage + kStreamPageWindow * 4 + kSliceTableInts * 4;
-    // Combine slots: four per row set (eight waves on one tile) or two per
-    // group (two groups of four waves).
-    const int64_t combine = 4 * (int64_t(rt) * ndt * 256 + int64_t(rt) * 32) * 4;
-    plan->lds_bytes = int32_t(ring > combine ? ring : combine);
+    // ring, page-id window and, for tile pairs, one softmax-state slot per tile
+    const int64_t pair_slot = (int64_t(rt) * ndt * 256 + int64_t(rt) * 32) * 4;
+    plan->lds_bytes = int32_t(ns * stage + kStreamPageWindow * 4 + (wk - 1) * int64_t(wr) * pair_slot);
   } else {
     const int64_t lds_v = (p->kv_dtype == VAT_F32) ? 0 : int64_t(kWaves) * kStepKeys * D * 2;
     int64_t lds_c = 0;

@@ -13,12 +13,12 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 // Row-tiled kernel: keys each wave consumes per step (two 16-key MFMA tiles).
 constexpr int kStepKeys = 32;
-// Streaming kernel: eight waves (two groups of four); keys per LDS stage (one
-// 16-key MFMA tile per wave of a group), most query rows per KV head it takes
-// (six 16-row tiles, three per group), LDS its stage ring may fill.
+// Streaming kernel: eight waves; keys per LDS stage (four 16-key MFMA tiles),
+// most 16-row tiles per KV head it takes (one or two per wave), LDS its stage
+// ring may fill.
 constexpr int kStreamThreads = 512;
 constexpr int kStageKeys = 64;
-constexpr int kStreamMaxTiles = 6;
+constexpr int kStreamMaxTiles = 16;
 constexpr int kStreamLdsBudget = 128 * 1024;
 // Page ids the streaming kernel keeps in LDS at a time.
 constexpr int kStreamPageWindow = 2048;
@@ -30,14 +30,9 @@ constexpr int kMergeThreads = 256;
 constexpr int kChunkQuantum = 16;
 constexpr int kMinChunkKeys = 128;
 constexpr int kMaxChunkKeys = 2048;
-// Batches up to this size are scheduled as balanced key slices (one wave
-// scans the requests' lengths).
+// Batches up to this size are scheduled as balanced slices of the page-index
+// space (a wave holds one request per lane).
 constexpr int kSliceMaxBatch = 64;
-// Request key ranges are padded to this many keys in the slice layout.
-constexpr int kSliceAlign = 16;
-// LDS table of the slice schedule: eight int fields per request.
-constexpr int kSliceTableInts = 8 * kSliceMaxBatch;
-static_assert(kSliceMaxBatch == 64, "one request per lane of a wave64");
 // Largest draft count per request a bit-packed mask may carry (one 64-bit
 // register holds a row).
 constexpr int kMaxMaskedLen = 64;
@@ -63,7 +58,7 @@ struct PartialArgs {
   int32_t page_shift, num_pages, num_kv_indices, num_mask_bytes;
   int32_t rows_per_block, row_blocks, waves_rows, waves_keys;
   int32_t chunk_keys, num_ids, has_mask;
-  int32_t slices;  // > 0: balanced key slices per KV head (streaming kernel, B <= 64)
+  int32_t slices;  // > 0: balanced page slices per KV head (streaming kernel, B <= 64)
 };
 
 // Arguments of the merge kernel.
@@ -79,7 +74,7 @@ struct MergeArgs {
   int32_t batch, hq, hkv, group, tokens;
   int32_t page_shift, num_kv_indices;
   int32_t rows_per_block, row_blocks, chunk_keys, num_ids, row_groups;
-  int32_t slices;  // > 0: partials come from balanced key slices, slot = slice + request
+  int32_t slices;  // > 0: partials come from balanced page slices, slot = slice + request
 };
 
 // Shape validation (host-detectable errors only).

@@ -1,19 +1,21 @@
 // Streaming partial kernel for verify shapes (bf16 or fp8 e4m3 caches, at
-// most 96 query rows per KV head).
+// most 256 query rows per KV head).
 //
-// One workgroup (eight wave64s, two per SIMD) per (chunk of a request's keys,
-// KV head). It holds all G * L_b query rows of the KV head (row r = t * G + g),
-// so every key and value of the chunk is read from HBM once per KV head
-// (flashmap page "sglang/verify_attention.py", module docstring: all G query
-// heads of a KV head in one program). The chunk is streamed through a ring of
-// 64-key LDS stages filled by gfx950's direct global->LDS 16-byte loads
+// One workgroup (eight wave64s, two per SIMD) per (work item, KV head). It
+// holds all G * L_b query rows of the KV head (row r = t * G + g), so every
+// key and value is read from HBM once per KV head (flashmap page
+// "sglang/verify_attention.py", module docstring: all G query heads of a KV
+// head in one program). A work item is either a balanced slice of the
+// page-index space, holding the segments of the requests whose pages fall in
+// it, or one chunk of one request. Its keys stream through a ring of 64-key
+// LDS stages filled by gfx950's direct global->LDS 16-byte loads
 // (global_load_lds_dwordx4), gathered page by page through the page table
 // (FlashInfer page "feat: Separate Q and KV dtypes for decode", paged layout);
-// the ring keeps several stages in flight without holding them in registers.
+// the ring runs on across segment boundaries, so a slice pays the start-up
+// latency once however many requests it touches.
 //
-// The eight waves form two groups of four. In a group, wave k owns the k-th
-// 16-key tile of a stage. With two or more 16-row tiles the groups split the
-// row tiles; with a single tile they take alternate stages. Per wave and tile:
+// Wave w computes row tiles [w RT, w RT + RT) over every key of a segment, so
+// its softmax state never has to be combined with another wave's:
 //   S^T = K . Q^T      v_mfma_f32_16x16x32_bf16 (A = K from LDS, B = Q^T in VGPRs)
 //   online softmax     base 2, one running max per row, raised lazily
 //   O^T += V^T . P^T   v_mfma_f32_16x16x16_bf16 (A = V^T read with the LDS
@@ -22,9 +24,9 @@
 // fp8 keys and values are decoded to bf16 in registers (exactly) right after
 // the LDS reads. The draft block at the end of the request is masked in place:
 // draft j is visible to token t iff j <= t (causal) or mask bit (t, j) is set.
-// The waves' partial results are combined through LDS; a chunk that is its
-// request's only one writes out and lse, otherwise a normalised fp32 partial
-// and its base-2 log-sum-exp go to the workspace for the merge.
+// A segment that is a whole request writes out and lse; otherwise a
+// normalised fp32 partial and its base-2 log-sum-exp go to the workspace for
+// the merge.
 #include <utility>
 
 #include "device_common.h"
@@ -32,20 +34,20 @@
 namespace vat {
 
 constexpr int kSWaves = kStreamThreads / 64;  // 8
-constexpr int kGroupWaves = 4;
 
-template <int KV, int D>
+// DW: waves issuing the DMA (4: the last four of eight; 8: all of them).
+template <int KV, int D, int DW = kSWaves>
 struct StreamGeom {
   static constexpr int EB = (KV == KV_E4M3) ? 1 : 2;  // bytes per cache element
   static constexpr int ROW = D * EB;                   // bytes per key row
   static constexpr int CPK = ROW / 16;                 // 16-byte chunks per key row
   static constexpr int KPI = 64 / CPK;                 // keys per 1 KB DMA instruction
   static constexpr int NINST = kStageKeys / KPI;       // DMA instructions per K (or V) block
-  static constexpr int IPW = NINST / kSWaves;          // per wave per block
-  static constexpr int NPW = 2 * IPW;                  // per wave per stage (K and V)
+  static constexpr int IPW = NINST / DW;               // per DMA wave per block
+  static constexpr int NPW = 2 * IPW;                  // per DMA wave per stage (K and V)
   static constexpr int BLK = kStageKeys * ROW;         // bytes of one K (or V) block
   static constexpr int STAGE = 2 * BLK;
-  static_assert(IPW >= 1 && NINST % kSWaves == 0, "stage must split over the waves");
+  static_assert(IPW >= 1 && NINST % DW == 0, "stage must split over the DMA waves");
 };
 
 // LDS position of 16-byte chunk c of stage-local key kl: chunks are XOR
@@ -81,36 +83,24 @@ __device__ __forceinline__ unsigned cvt_pk_bf16(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------------------
-// The chunk's page ids are staged in LDS (kStreamPageWindow entries from
-// request page `base` on), so the DMA issue reads them with LDS loads and never
-// waits on the vector-memory counter that paces the stage ring.
-__device__ __forceinline__ int page_id(const PartialArgs& a, const Req& r, int rel_page) {
-  const int idx = clampi(r.kv_start + clampi(rel_page, 0, max(r.pages - 1, 0)), 0,
-                         max(a.num_kv_indices - 1, 0));
-  return clampi(a.kv_indices[idx], 0, a.num_pages - 1);
-}
-
-__device__ __forceinline__ void fill_page_window(int* win, const PartialArgs& a, const Req& r,
-                                                 int base, int last_page) {
-  const int n = min(kStreamPageWindow, last_page - base + 1);
-  for (int i = threadIdx.x; i < n; i += kStreamThreads) win[i] = page_id(a, r, base + i);
-}
-
+// Page ids of the work item live in an LDS window (kStreamPageWindow entries),
+// so the DMA issue reads them with LDS loads and never waits on the
+// vector-memory counter that paces the stage ring.
 // Issue this wave's share of the DMA loads of one stage: keys n0 .. n0 + 63,
 // each clamped to `last` (the item's last key) so every address is a real
 // cached entry; keys past the item are masked out of the softmax later.
-template <int KV, int D>
+template <int KV, int D, int DW>
 __device__ __forceinline__ void issue_stage(const PartialArgs& a, const int* win, int win_base,
                                             int last_rel, int h, int n0, int last,
-                                            unsigned char* stage, int wave, int lane,
+                                            unsigned char* stage, int dw, int lane,
                                             bool uniform_pages) {
-  using G = StreamGeom<KV, D>;
+  using G = StreamGeom<KV, D, DW>;
   const int ps_mask = (1 << a.page_shift) - 1;
   const long long page_bytes = (long long)G::ROW * a.hkv << a.page_shift;
   int pg[G::IPW];
 #pragma unroll
   for (int ii = 0; ii < G::IPW; ++ii) {
-    const int i = wave * G::IPW + ii;
+    const int i = dw * G::IPW + ii;
     const int n = min(n0 + i * G::KPI + lane / G::CPK, last);
     const int first = min(n0 + i * G::KPI, last);
     const int rel = uniform_pages ? (first >> a.page_shift) - win_base : (n >> a.page_shift) - win_base;
@@ -118,7 +108,7 @@ __device__ __forceinline__ void issue_stage(const PartialArgs& a, const int* win
   }
 #pragma unroll
   for (int ii = 0; ii < G::IPW; ++ii) {
-    const int i = wave * G::IPW + ii;
+    const int i = dw * G::IPW + ii;
     const int kl = i * G::KPI + lane / G::CPK;
     const int c = swz<G::CPK>(kl, lane % G::CPK);
     const int n = min(n0 + kl, last);
@@ -176,311 +166,314 @@ struct Vis {
   int has_mask;
 };
 
-template <int KV, int D, int RT>
+// An empty volatile asm statement: the rare branch it sits in (masking of the
+// boundary stages, rescaling) stays a branch instead of being flattened into
+// selects that would run on every stage.
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
+
+// One 64-key stage against this wave's RT row tiles. The four 16-key tiles
+// are processed together: their S^T MFMAs interleave, the softmax takes one
+// row max over all 64 keys, and the V^T reads of tile kt + 1 are in flight
+// while tile kt's PV MFMAs run.
+// KT: 16-key tiles this wave takes, tiles kt0 .. kt0 + KT - 1 of the stage.
+template <int KV, int D, int RT, int KT>
 __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsigned (&qf)[RT][D / 8],
                                               const int (&row_t)[RT],
                                               const unsigned long long (&row_bits)[RT],
                                               const Vis& vis, const unsigned char* stage, int n0,
-                                              float c, int kw, int lane) {
+                                              float c, int lane, int kt0) {
   using G = StreamGeom<KV, D>;
+  static_assert(KT == 2 || KT == 4, "one or two 32-key blocks");
+  constexpr int NDT = D / 16;
   const int l16 = lane & 15;
   const int j4 = lane >> 4;
-  // ---- S^T tile of this wave's 16 keys against its row tiles
-  f32x4 st[RT];
+  // ---- S^T tiles: lane (key 16 kt + l % 16 as A row, query row l % 16 as
+  // B column) accumulates over 32-wide d steps.
+  f32x4 st[KT][RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) st[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int klk = 16 * kw + l16;
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) st[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
-    u32x4 kw4;
-    if constexpr (KV == KV_E4M3) {
-      const int ch = 4 * (ks >> 1) + j4;
-      const u32x2 raw = *(const u32x2*)(stage + klk * G::ROW + (swz<G::CPK>(klk, ch) << 4) + 8 * (ks & 1));
-      kw4 = e4m3x8_to_bf16(raw.x, raw.y);
-    } else {
-      const int ch = 4 * ks + j4;
-      kw4 = *(const u32x4*)(stage + klk * G::ROW + (swz<G::CPK>(klk, ch) << 4));
-    }
-    const bf16x8 ka = __builtin_bit_cast(bf16x8, kw4);
+    bf16x8 ka[KT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const u32x4 qw = {qf[rt][4 * ks], qf[rt][4 * ks + 1], qf[rt][4 * ks + 2], qf[rt][4 * ks + 3]};
-      st[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, __builtin_bit_cast(bf16x8, qw), st[rt], 0, 0, 0);
+    for (int kt = 0; kt < KT; ++kt) {
+      const int klk = 16 * (kt0 + kt) + l16;
+      u32x4 kw4;
+      if constexpr (KV == KV_E4M3) {
+        const int ch = 4 * (ks >> 1) + j4;
+        const u32x2 raw =
+            *(const u32x2*)(stage + klk * G::ROW + (swz<G::CPK>(klk, ch) << 4) + 8 * (ks & 1));
+        kw4 = e4m3x8_to_bf16(raw.x, raw.y);
+      } else {
+        const int ch = 4 * ks + j4;
+        kw4 = *(const u32x4*)(stage + klk * G::ROW + (swz<G::CPK>(klk, ch) << 4));
+      }
+      ka[kt] = __builtin_bit_cast(bf16x8, kw4);
     }
-  }
-  // ---- keys past the item, drafts under causal / mask
-  const int nw = n0 + 16 * kw + 4 * j4;  // this lane's first key
-  if (n0 + kStageKeys > vis.hi || n0 + kStageKeys > vis.masked_from) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int n = nw + e;
-      const int jd = n - vis.masked_from;
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        bool ok = n < vis.hi;
-        if (jd >= 0) {
-          if (vis.has_mask) ok = ok && jd < 64 && ((row_bits[rt] >> jd) & 1ull);
-          else ok = ok && jd <= row_t[rt];
-        }
-        if (!ok) st[rt][e] = kNegInf;
+        const u32x4 qw = {qf[rt][4 * ks], qf[rt][4 * ks + 1], qf[rt][4 * ks + 2], qf[rt][4 * ks + 3]};
+        st[kt][rt] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kt], __builtin_bit_cast(bf16x8, qw), st[kt][rt], 0, 0, 0);
       }
-    }
+  }
+  // ---- keys past the item, drafts under causal / mask. Lane (row, j) holds
+  // keys 16 kt + 4 j + e.
+  if (n0 + kStageKeys > vis.hi || n0 + kStageKeys > vis.masked_from) {
+    keep_branch();
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n = n0 + 16 * (kt0 + kt) + 4 * j4 + e;
+        const int jd = n - vis.masked_from;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          bool ok = n < vis.hi;
+          if (jd >= 0) {
+            if (vis.has_mask) ok = ok && jd < 64 && ((row_bits[rt] >> jd) & 1ull);
+            else ok = ok && jd <= row_t[rt];
+          }
+          if (!ok) st[kt][rt][e] = kNegInf;
+        }
+      }
   }
   // ---- online softmax (base 2); p replaces the logits. The running max is
-  // raised only when a tile's max exceeds it by more than kRescaleSlack, so
-  // the accumulators are rescaled rarely; p = 2^(s c - m) then stays below
+  // raised only when the stage's max exceeds it by more than kRescaleSlack,
+  // so the accumulators are rescaled rarely; p = 2^(s c - m) then stays below
   // 2^kRescaleSlack, and out and lse use the same m, so the result is exact.
+  s16x4 pb[KT][RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    float mx = fmaxf(fmaxf(st[rt][0], st[rt][1]), fmaxf(st[rt][2], st[rt][3]));
+    float mx = kNegInf;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+      mx = fmaxf(mx, fmaxf(fmaxf(st[kt][rt][0], st[kt][rt][1]), fmaxf(st[kt][rt][2], st[kt][rt][3])));
     mx = rowmax4_v(mx) * c;
     const bool grow = mx > acc.m[rt] + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(grow)) {
+      keep_branch();
       const float m_new = grow ? mx : acc.m[rt];
       const float alpha = grow ? fast_exp2(acc.m[rt] - m_new) : 1.f;  // 0 when m was -inf
       acc.l[rt] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) acc.o[rt][dt] *= alpha;
+      for (int dt = 0; dt < NDT; ++dt) acc.o[rt][dt] *= alpha;
       acc.m[rt] = m_new;
     }
     // Rows that have seen nothing keep m = -inf; base 0 gives p = 0 for them.
     const float base = (acc.m[rt] == kNegInf) ? 0.f : acc.m[rt];
     float sum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p = fast_exp2(__builtin_fmaf(st[rt][e], c, -base));
-      st[rt][e] = p;
-      sum += p;
+    for (int kt = 0; kt < KT; ++kt) {
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[e] = fast_exp2(__builtin_fmaf(st[kt][rt][e], c, -base));
+        sum += p[e];
+      }
+      pb[kt][rt] = __builtin_bit_cast(s16x4, u32x2{cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3])});
     }
     acc.l[rt] += sum;
   }
-  // ---- O^T += V^T . P^T
-  s16x4 pb[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-    pb[rt] = __builtin_bit_cast(s16x4, u32x2{cvt_pk_bf16(st[rt][0], st[rt][1]),
-                                             cvt_pk_bf16(st[rt][2], st[rt][3])});
+  // ---- O^T += V^T . P^T, 32 keys per v_mfma_f32_16x16x32_bf16. Its k index
+  // 8 j + e (lane group j) stands for key 4 j + e of tile 2 kb (e < 4) or key
+  // 4 j + e - 4 of tile 2 kb + 1: the same order in both operands, so the
+  // S^T tiles serve as P^T without moving, and V^T takes one 4-key read per
+  // tile (the contraction does not depend on the order of k).
+  auto mfma32 = [](s16x4 v_lo, s16x4 v_hi, s16x4 p_lo, s16x4 p_hi, f32x4 c) {
+    const u32x2 a0 = __builtin_bit_cast(u32x2, v_lo), a1 = __builtin_bit_cast(u32x2, v_hi);
+    const u32x2 b0 = __builtin_bit_cast(u32x2, p_lo), b1 = __builtin_bit_cast(u32x2, p_hi);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y}),
+                                                   __builtin_bit_cast(bf16x8, u32x4{b0.x, b0.y, b1.x, b1.y}),
+                                                   c, 0, 0, 0);
+  };
   const unsigned char* vb = stage + G::BLK;
-  constexpr int NDT = D / 16;
   if constexpr (KV == KV_E4M3) {
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      // Lane (d = l % 16, j = l / 16): codes of keys 16 kw + 4 j + e at d.
-      const int kl0 = 16 * kw + 4 * j4;
+    // Lane (d = l % 16, j = l / 16): codes of keys 16 kt + 4 j + e at d,
+    // decoded exactly to bf16.
+    auto vfrag = [&](int kt, int dt) {
+      const int kl0 = 16 * (kt0 + kt) + 4 * j4;
       const int byte = 16 * dt + l16;
       const int ch = byte >> 4, within = byte & 15;
       unsigned b[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        b[e] = vb[(kl0 + e) * G::ROW + (swz<G::CPK>(kl0 + e, ch) << 4) + within];
+      for (int e = 0; e < 4; ++e) b[e] = vb[(kl0 + e) * G::ROW + (swz<G::CPK>(kl0 + e, ch) << 4) + within];
       const unsigned packed = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-      const s16x4 va = __builtin_bit_cast(
-          s16x4, u32x2{e4m3x2_to_bf16x2(packed, false), e4m3x2_to_bf16x2(packed, true)});
+      return __builtin_bit_cast(s16x4, u32x2{e4m3x2_to_bf16x2(packed, false), e4m3x2_to_bf16x2(packed, true)});
+    };
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        acc.o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[rt], acc.o[rt][dt], 0, 0, 0);
-    }
+    for (int kb = 0; kb < KT / 2; ++kb)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const s16x4 v0 = vfrag(2 * kb, dt), v1 = vfrag(2 * kb + 1, dt);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          acc.o[rt][dt] = mfma32(v0, v1, pb[2 * kb][rt], pb[2 * kb + 1][rt], acc.o[rt][dt]);
+      }
   } else {
     // Transpose loads: source lane s of each 16-lane group points at the 8
-    // bytes V[key 16 kw + 4 j + s / 4][d = 16 dt + 4 (s % 4) ..]; lane (d, j)
-    // then receives V[16 kw + 4 j + e][16 dt + d], e = 0..3. All NDT reads
-    // are issued first; tile dt waits only for its own.
-    const int kl = 16 * kw + 4 * j4 + (l16 >> 2);
-    s16x4 va[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
+    // bytes V[key 16 kt + 4 j + s / 4][d = 16 dt + 4 (s % 4) ..]; lane (d, j)
+    // then receives V[16 kt + 4 j + e][16 dt + d], e = 0..3. Each MFMA waits
+    // only for its own reads (LDS reads complete in order).
+    const int klb = 4 * j4 + (l16 >> 2);
+    auto vaddr = [&](int kt, int dt) {
+      const int kl = 16 * (kt0 + kt) + klb;
       const int d0 = 16 * dt + 4 * (l16 & 3);
-      const int ch = d0 >> 3;
-      va[dt] = lds_read_tr16(vb + kl * G::ROW + (swz<G::CPK>(kl, ch) << 4) + (d0 & 7) * 2);
+      return vb + kl * G::ROW + (swz<G::CPK>(kl, d0 >> 3) << 4) + (d0 & 7) * 2;
+    };
+    s16x4 v0[NDT], v1[NDT], v2[NDT], v3[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) v0[dt] = lds_read_tr16(vaddr(0, dt));
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) v1[dt] = lds_read_tr16(vaddr(1, dt));
+    // With two blocks and one row tile the third tile's reads go out before
+    // the first block's MFMAs.
+    constexpr bool kAhead = KT == 4 && RT == 1;
+    if constexpr (kAhead) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) v2[dt] = lds_read_tr16(vaddr(2, dt));
     }
     [&]<int... I>(std::integer_sequence<int, I...>) {
-      ((lds_wait_tied<NDT - 1 - I>(va[I]),
+      ((lds_wait_tied2<(kAhead ? NDT : 0) + NDT - 1 - I>(v0[I], v1[I]),
         [&] {
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
-            acc.o[rt][I] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[I], pb[rt], acc.o[rt][I], 0, 0, 0);
+          for (int rt = 0; rt < RT; ++rt) acc.o[rt][I] = mfma32(v0[I], v1[I], pb[0][rt], pb[1][rt], acc.o[rt][I]);
         }()),
        ...);
     }(std::make_integer_sequence<int, NDT>{});
-  }
-}
-
-// Combine the partial (m, l, o) of waves that hold the same rows: waves
-// [0, n) of the set fold into wave 0 through LDS slots, halving each round.
-template <int D, int RT>
-__device__ __forceinline__ void combine_waves(StreamAcc<D, RT>& acc, float* slots, int set,
-                                              int idx, int n, int lane) {
-  constexpr int NDT = D / 16;
-  constexpr int SLOT = RT * NDT * 256 + RT * 32;  // floats
-  const int l16 = lane & 15, j4 = lane >> 4;
-  for (int half = n / 2; half >= 1; half /= 2) {
-    __syncthreads();
-    if (idx >= half && idx < 2 * half) {
-      float* sl = slots + (set * (n / 2) + (idx - half)) * SLOT;
+    if constexpr (KT == 4) {
+      if constexpr (!kAhead) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) *(f32x4*)(sl + ((rt * NDT + dt) * 64 + lane) * 4) = acc.o[rt][dt];
-        if (j4 == 0) {
-          sl[RT * NDT * 256 + rt * 32 + l16] = acc.m[rt];
-          sl[RT * NDT * 256 + rt * 32 + 16 + l16] = acc.l[rt];
-        }
+        for (int dt = 0; dt < NDT; ++dt) v2[dt] = lds_read_tr16(vaddr(2, dt));
       }
-    }
-    __syncthreads();
-    if (idx < half) {
-      const float* sl = slots + (set * (n / 2) + idx) * SLOT;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const float mb = sl[RT * NDT * 256 + rt * 32 + l16];
-        const float lb = sl[RT * NDT * 256 + rt * 32 + 16 + l16];
-        const float m = fmaxf(acc.m[rt], mb);
-        const float base = (m == kNegInf) ? 0.f : m;
-        const float wa = fast_exp2(acc.m[rt] - base);
-        const float wb = fast_exp2(mb - base);
+      for (int dt = 0; dt < NDT; ++dt) v3[dt] = lds_read_tr16(vaddr(3, dt));
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((lds_wait_tied2<NDT - 1 - I>(v2[I], v3[I]),
+          [&] {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const f32x4 ob = *(const f32x4*)(sl + ((rt * NDT + dt) * 64 + lane) * 4);
-          acc.o[rt][dt] = acc.o[rt][dt] * wa + ob * wb;
-        }
-        acc.l[rt] = acc.l[rt] * wa + lb * wb;
-        acc.m[rt] = m;
-      }
+            for (int rt = 0; rt < RT; ++rt) acc.o[rt][I] = mfma32(v2[I], v3[I], pb[2][rt], pb[3][rt], acc.o[rt][I]);
+          }()),
+         ...);
+      }(std::make_integer_sequence<int, NDT>{});
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// One segment of work: keys [lo, hi) of request b for KV head h, all of its
-// query rows. `final_write`: the segment is the whole request, so out and lse
-// are written; otherwise partial slot `slot` is.
-// RT: 16-row tiles per wave. ALT: one row tile, the two wave groups take
-// alternate stages; otherwise group g holds row tiles [g RT, g RT + RT).
-template <int KV, int D, int RT, int NS, bool ALT>
-__device__ __forceinline__ void process_segment(const PartialArgs& a, const Req& r, int lo, int hi,
-                                                bool final_write, int slot, int h,
-                                                unsigned char* smem, int wave, int lane) {
-  using G = StreamGeom<KV, D>;
-  const int grp = wave / kGroupWaves;
-  const int kw = wave % kGroupWaves;
-  const int l16 = lane & 15;
-  const int j4 = lane >> 4;
-  const int R = a.group * r.L;
-  Vis vis{hi, r.prefix, a.has_mask};
-  const int last = max(hi - 1, 0);
-  const int nst = hi > lo ? (hi - lo + kStageKeys - 1) / kStageKeys : 0;
+// The workgroup's segments, one per lane: segment i is keys [lo, hi) of one
+// request. Its stages are numbered end to end across segments: segment i owns
+// global stages [incl - nst, incl). `woff` is the page-window index of the
+// request's page 0 (window index = position in kv_indices minus the window's
+// first position).
+struct SegLane {
+  int lo = 0, hi = 0, nst = 0, incl = 0;
+  int woff = 0, q_start = 0, L = 0, prefix = 0, mask_off = 0, slot = 0, whole = 0;
+};
 
-  // ---- rows: tile rt of this wave, lane row row0 + rt * 16 + l16
-  const int row0 = ALT ? 0 : grp * RT * 16;
+__device__ __forceinline__ int lane_val(int v, int i) { return __builtin_amdgcn_readlane(v, i); }
+
+// Window page ids: entries [base, base + n) of the window range starting at
+// kv_indices position w0, clamped to real pages.
+__device__ __forceinline__ void fill_window(int* win, const PartialArgs& a, int w0, int base, int count) {
+  const int n = min(kStreamPageWindow, count - base);
+  for (int i = threadIdx.x; i < n; i += kStreamThreads)
+    win[i] = clampi(a.kv_indices[w0 + base + i], 0, a.num_pages - 1);
+}
+
+// One wave's rows of a segment: Q^T operand fragments and mask rows. The
+// loads are issued by fetch() and used only after the caller's wait, so no
+// load is left for the compiler to wait on where the stages are computed:
+// the mask bytes stay raw until finish().
+template <int KV, int D, int RT>
+struct RowSet {
   int row_t[RT], row_g[RT];
   bool row_ok[RT];
   unsigned long long row_bits[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = row0 + rt * 16 + l16;
-    row_t[rt] = row / a.group;
-    row_g[rt] = row % a.group;
-    row_ok[rt] = row < R;
-    row_bits[rt] = 0;
-    if (a.has_mask && row_ok[rt])
-      row_bits[rt] = load_mask_row(a.mask, a.num_mask_bytes, r.mask_off, row_t[rt], r.L);
-  }
-  // Q^T operand: lane (row, j) holds d = qk_d(ks, j) .. +7 for each 32-wide step ks.
   unsigned qf[RT][D / 8];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const long long qrow =
-        ((long long)(r.q_start + min(row_t[rt], r.L - 1)) * a.hq + h * a.group + row_g[rt]) * D;
-    const unsigned short* qp = (const unsigned short*)a.q + qrow;
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      const int d0 = (KV == KV_E4M3) ? 64 * (ks >> 1) + 16 * j4 + 8 * (ks & 1) : 32 * ks + 8 * j4;
-      const u32x4 x = row_ok[rt] ? *(const u32x4*)(qp + d0) : u32x4{0, 0, 0, 0};
-      qf[rt][4 * ks] = x.x;
-      qf[rt][4 * ks + 1] = x.y;
-      qf[rt][4 * ks + 2] = x.z;
-      qf[rt][4 * ks + 3] = x.w;
-    }
-  }
-  // ---- page ids of the segment into LDS. The Q and mask loads above are in
-  // flight meanwhile; all of them have landed once this returns, so the ring
-  // below starts with no register load outstanding (a load still pending
-  // there would make every stage wait for all of its queued DMA).
-  int* win = (int*)(smem + NS * G::STAGE);
-  const int last_page = last >> a.page_shift;
-  int win_base = lo >> a.page_shift;
-  if (nst > 0) fill_page_window(win, a, r, win_base, last_page);
-  wait_vmcnt<0>();
+  unsigned raw[RT][9];  // mask bytes from the row's first byte on
 
-  // A group whose tiles hold no row skips the math (it still issues loads).
-  const bool has_rows = row0 < R;
-
-  StreamAcc<D, RT> acc;
+  __device__ __forceinline__ void fetch(const PartialArgs& a, int q_start, int L, int mask_off,
+                                        int row0, int h, int lane) {
+    const int l16 = lane & 15, j4 = lane >> 4;
+    const int R = a.group * L;
+    const int last = max(a.num_mask_bytes - 1, 0);
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    acc.m[rt] = kNegInf;
-    acc.l[rt] = 0.f;
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = row0 + rt * 16 + l16;
+      row_t[rt] = row / a.group;
+      row_g[rt] = row % a.group;
+      row_ok[rt] = row < R;
+      // Q^T operand: lane (row, j) holds d = qk_d(ks, j) .. +7 for each 32-wide step ks.
+      const long long qrow =
+          ((long long)(q_start + min(row_t[rt], L - 1)) * a.hq + h * a.group + row_g[rt]) * D;
+      const unsigned short* qp = (const unsigned short*)a.q + qrow;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) acc.o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // ---- the stage ring
-  // Iteration s: wait for this wave's stage-s loads, barrier (everyone's
-  // stage-s loads have landed and every wave is done with stage s - 1),
-  // refill the buffer of stage s - 1 with stage s + NS - 1, compute stage s.
-  // The barrier after the page-window fill also keeps a previous segment's
-  // combine slots (which alias the stage buffers) safe from the new loads.
-  __syncthreads();
-  if (nst > 0) {
-    const bool uniform_pages = (1 << a.page_shift) >= G::KPI;
-    auto issue = [&](int s) {
-      const int n0 = lo + s * kStageKeys;
-      const int p_hi = min(n0 + kStageKeys - 1, last) >> a.page_shift;
-      if (p_hi - win_base >= kStreamPageWindow) {
-        // Long segment: move the window (drains the ring; once per window).
-        wait_vmcnt<0>();
-        __syncthreads();
-        win_base = min(n0, last) >> a.page_shift;
-        fill_page_window(win, a, r, win_base, last_page);
-        __syncthreads();
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const int d0 = (KV == KV_E4M3) ? 64 * (ks >> 1) + 16 * j4 + 8 * (ks & 1) : 32 * ks + 8 * j4;
+        const u32x4 x = *(const u32x4*)(qp + d0);
+        qf[rt][4 * ks] = x.x;
+        qf[rt][4 * ks + 1] = x.y;
+        qf[rt][4 * ks + 2] = x.z;
+        qf[rt][4 * ks + 3] = x.w;
       }
-      issue_stage<KV, D>(a, win, win_base, min(last_page - win_base, kStreamPageWindow - 1), h, n0,
-                         last, smem + (s % NS) * G::STAGE, wave, lane, uniform_pages);
-    };
-    for (int s = 0; s < NS - 1; ++s)
-      if (s < nst) issue(s);
-    for (int s = 0; s < nst; ++s) {
-      wait_stage<G::NPW, NS>(min(NS - 2, nst - 1 - s));
-      __builtin_amdgcn_s_barrier();
-      if (s + NS - 1 < nst) issue(s + NS - 1);
-      if (has_rows && (!ALT || (s & 1) == grp))
-        compute_stage<KV, D, RT>(acc, qf, row_t, row_bits, vis, smem + (s % NS) * G::STAGE,
-                                 lo + s * kStageKeys, a.c_log2, kw, lane);
+      // Row t of the packed L x L block starts at bit t L; L <= 64 bits span
+      // at most nine bytes (indices clamped to the mask buffer).
+      if (a.has_mask) {
+        const int byte0 = mask_off + ((min(row_t[rt], L - 1) * L) >> 3);
+#pragma unroll
+        for (int i = 0; i < 9; ++i) raw[rt][i] = a.mask[clampi(byte0 + i, 0, last)];
+      }
     }
   }
+
+  __device__ __forceinline__ void finish(int L, bool has_mask) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) acc.l[rt] = rowsum4_v(acc.l[rt]);
+    for (int rt = 0; rt < RT; ++rt) {
+      if (!row_ok[rt]) {
+#pragma unroll
+        for (int k = 0; k < D / 8; ++k) qf[rt][k] = 0u;
+      }
+      row_bits[rt] = 0;
+      if (has_mask && row_ok[rt]) {
+        unsigned long long acc = 0;
+#pragma unroll
+        for (int i = 7; i >= 0; --i) acc = (acc << 8) | raw[rt][i];
+        const int sh = (row_t[rt] * L) & 7;
+        unsigned long long bits = acc >> sh;
+        if (sh) bits |= (unsigned long long)raw[rt][8] << (64 - sh);
+        if (L < 64) bits &= (1ull << L) - 1ull;
+        row_bits[rt] = bits;
+      }
+    }
+  }
+};
 
-  // ---- combine waves that hold the same rows
-  float* slots = (float*)smem;
-  if (ALT) combine_waves<D, RT>(acc, slots, 0, wave, kSWaves, lane);
-  else combine_waves<D, RT>(acc, slots, grp, kw, kGroupWaves, lane);
-  if (ALT ? wave != 0 : (kw != 0 || !has_rows)) return;
-
-  // ---- write: out (q dtype) and natural-log lse for a whole request;
-  // otherwise a normalised fp32 partial (v_scale not yet applied) and its
-  // base-2 log-sum-exp.
+// Write a finished segment's rows of this wave (`lrow`: the rows' full sums):
+// out (bf16) and natural-log lse for a whole request, otherwise a normalised
+// fp32 partial (v_scale not yet applied) and its base-2 log-sum-exp in slot
+// `slot`.
+template <int KV, int D, int RT>
+__device__ __forceinline__ void write_rows(const StreamAcc<D, RT>& acc, const float (&lrow)[RT],
+                                           const RowSet<KV, D, RT>& rs, const PartialArgs& a,
+                                           int q_start, bool whole, int slot, int row0, int h,
+                                           int lane) {
   constexpr int NDT = D / 16;
+  const int l16 = lane & 15, j4 = lane >> 4;
   const long long pid = (long long)slot * a.hkv + h;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    if (!row_ok[rt]) continue;
-    const float lsum = acc.l[rt];
+    const float lsum = lrow[rt];
+    if (!rs.row_ok[rt]) continue;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     const float lse2 = lsum > 0.f ? acc.m[rt] + fast_log2(lsum) : kNegInf;
     const int local = row0 + rt * 16 + l16;
-    if (final_write) {
-      const long long orow = (long long)(r.q_start + row_t[rt]) * a.hq + h * a.group + row_g[rt];
+    if (whole) {
+      const long long orow = (long long)(q_start + rs.row_t[rt]) * a.hq + h * a.group + rs.row_g[rt];
       unsigned short* op = (unsigned short*)a.out + orow * D;
       const float sc = inv * a.v_scale;
 #pragma unroll
@@ -498,97 +491,289 @@ __device__ __forceinline__ void process_segment(const PartialArgs& a, const Req&
   }
 }
 
-template <int KV, int D, int RT, int NS, bool ALT>
+// Softmax state of a row set in LDS, handed from the second wave of a tile
+// pair to the first: O^T tiles as the lanes hold them, then the rows' running
+// max and full sum.
+template <int D, int RT>
+struct PairSlot {
+  static constexpr int NDT = D / 16;
+  static constexpr int FLOATS = RT * NDT * 256 + RT * 32;
+};
+
+__device__ __forceinline__ void wait_lds_writes() {
+  // s_waitcnt lgkmcnt(0), vector-memory and export counts left alone
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+template <int D, int RT>
+__device__ __forceinline__ void store_pair_state(const StreamAcc<D, RT>& acc, float* slot, int lane) {
+  constexpr int NDT = D / 16;
+  const int l16 = lane & 15, j4 = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const float lrow = rowsum4_v(acc.l[rt]);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) *(f32x4*)(slot + ((rt * NDT + dt) * 64 + lane) * 4) = acc.o[rt][dt];
+    if (j4 == 0) {
+      slot[RT * NDT * 256 + rt * 16 + l16] = acc.m[rt];
+      slot[RT * NDT * 256 + RT * 16 + rt * 16 + l16] = lrow;
+    }
+  }
+  wait_lds_writes();
+}
+
+// Fold the partner's state into acc; lrow receives the combined row sums.
+template <int D, int RT>
+__device__ __forceinline__ void merge_pair_state(StreamAcc<D, RT>& acc, float (&lrow)[RT],
+                                                 const float* slot, bool partner, int lane) {
+  constexpr int NDT = D / 16;
+  const int l16 = lane & 15;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    lrow[rt] = rowsum4_v(acc.l[rt]);
+    if (!partner) continue;
+    const float mb = slot[RT * NDT * 256 + rt * 16 + l16];
+    const float lb = slot[RT * NDT * 256 + RT * 16 + rt * 16 + l16];
+    const float m = fmaxf(acc.m[rt], mb);
+    const float base = (m == kNegInf) ? 0.f : m;
+    const float wa = fast_exp2(acc.m[rt] - base);
+    const float wb = fast_exp2(mb - base);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      acc.o[rt][dt] = acc.o[rt][dt] * wa + *(const f32x4*)(slot + ((rt * NDT + dt) * 64 + lane) * 4) * wb;
+    lrow[rt] = lrow[rt] * wa + lb * wb;
+    acc.m[rt] = m;
+  }
+}
+
+// One workgroup per (work item, KV head). A work item is a balanced slice of
+// the page-index space (batches of at most 64 requests) or one chunk of one
+// request; either way a list of request segments whose 64-key stages flow
+// through one ring of LDS buffers filled by DMA. Wave w < waves_rows owns row
+// tiles [w RT, w RT + RT) of every segment and runs all of its keys, so no
+// two waves ever hold parts of the same row; all eight waves issue the DMA.
+template <int KV, int D, int RT, int NS, int DW, int P>
 __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
+  using G = StreamGeom<KV, D, DW>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  int* win = (int*)(smem + NS * G::STAGE);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int h = blockIdx.y;
-  ReqArrays ra{a.kv_indptr, a.last_page_len, a.qo_indptr, a.has_mask ? a.mask_indptr : nullptr,
-               a.batch, a.page_shift, a.chunk_keys, a.num_kv_indices, a.tokens};
-  Req r;
-  int lo, hi, slot;
-  bool whole;
-  if (a.slices == 0) {
-    // Chunks: work item blockIdx.x is chunk j of some request.
+  const int shift = a.page_shift;
+
+  // ---- the segment lanes and the page window: one round of loads for a slice
+  SegLane sg;
+  int w0, wcount;  // window range: kv_indices positions [w0, w0 + wcount)
+  if (a.slices > 0) {
+    const int per = (a.num_kv_indices + a.slices - 1) / a.slices;
+    w0 = blockIdx.x * per;
+    wcount = min(per, a.num_kv_indices - w0);
+    if (wcount <= 0) return;
+    // Page ids of the slice, requested with the request table below.
+    constexpr int PT = kStreamPageWindow / kStreamThreads;
+    int pid[PT];
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+      const int i = threadIdx.x + k * kStreamThreads;
+      pid[k] = i < min(wcount, kStreamPageWindow) ? a.kv_indices[w0 + i] : 0;
+    }
+    const bool in = lane < a.batch;
+    const int i = in ? lane : 0;
+    const Req r = make_req(a.kv_indptr[i], a.kv_indptr[i + 1], in ? a.last_page_len[i] : 1,
+                           a.qo_indptr[i], a.qo_indptr[i + 1],
+                           (a.has_mask && in) ? a.mask_indptr[i] : 0, shift, a.num_kv_indices,
+                           a.tokens);
+    const int p0 = max(r.kv_start, w0), p1 = min(r.kv_start + r.pages, w0 + wcount);
+    if (in && r.L > 0 && p0 < p1) {
+      sg.lo = (p0 - r.kv_start) << shift;
+      sg.hi = min((p1 - r.kv_start) << shift, r.kv_len);
+      sg.nst = (sg.hi - sg.lo + kStageKeys - 1) / kStageKeys;
+      sg.woff = r.kv_start - w0;
+      sg.q_start = r.q_start;
+      sg.L = r.L;
+      sg.prefix = r.prefix;
+      sg.mask_off = r.mask_off;
+      sg.slot = blockIdx.x + lane;
+      sg.whole = sg.lo == 0 && sg.hi == r.kv_len;
+    }
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+      const int i2 = threadIdx.x + k * kStreamThreads;
+      if (i2 < min(wcount, kStreamPageWindow)) win[i2] = clampi(pid[k], 0, a.num_pages - 1);
+    }
+  } else {
+    // Chunk j of the request owning work item blockIdx.x: one segment (lane 0).
+    ReqArrays ra{a.kv_indptr, a.last_page_len, a.qo_indptr, a.has_mask ? a.mask_indptr : nullptr,
+                 a.batch, shift, a.chunk_keys, a.num_kv_indices, a.tokens};
+    Req r;
     Item it;
     if (!find_item(ra, blockIdx.x, lane, r, it) || r.L == 0) return;
-    lo = it.j * a.chunk_keys;
-    hi = min(lo + a.chunk_keys, r.kv_len);
-    whole = chunk_count(r.kv_len, a.chunk_keys) == 1;
-    slot = it.slot;
-    process_segment<KV, D, RT, NS, ALT>(a, r, lo, hi, whole, slot, h, smem, wave, lane);
-    return;
-  }
-  // Balanced slices: workgroup x takes [x per, (x + 1) per) of the
-  // concatenated key range, request segment by request segment. Every wave
-  // scans the lengths; wave 0 leaves the table in LDS (past the page window)
-  // so nothing per-request stays in registers across segments (field k of
-  // request i at tab[64 k + i]).
-  int* tab = (int*)(smem + NS * StreamGeom<KV, D>::STAGE + kStreamPageWindow * 4);
-  int b, x0, x1;
-  {
-    SliceLanes sl;
-    slice_lanes(ra, a.slices, lane, sl);
-    x0 = blockIdx.x * sl.per;
-    x1 = min(x0 + sl.per, sl.total);
-    b = __popcll(__ballot(lane < a.batch && sl.cum + sl.n <= x0));
-    if (wave == 0) {
-      tab[0 * 64 + lane] = sl.ip0;
-      tab[1 * 64 + lane] = sl.ip1;
-      tab[2 * 64 + lane] = sl.lp;
-      tab[3 * 64 + lane] = sl.q0;
-      tab[4 * 64 + lane] = sl.q1;
-      tab[5 * 64 + lane] = sl.mo;
-      tab[6 * 64 + lane] = sl.cum;
-      tab[7 * 64 + lane] = sl.n;
+    const int lo = it.j * a.chunk_keys;
+    const int hi = min(lo + a.chunk_keys, r.kv_len);
+    if (lo >= hi) return;
+    w0 = r.kv_start + (lo >> shift);
+    wcount = ((hi - 1) >> shift) - (lo >> shift) + 1;
+    if (lane == 0) {
+      sg.lo = lo;
+      sg.hi = hi;
+      sg.nst = (hi - lo + kStageKeys - 1) / kStageKeys;
+      sg.woff = r.kv_start - w0;
+      sg.q_start = r.q_start;
+      sg.L = r.L;
+      sg.prefix = r.prefix;
+      sg.mask_off = r.mask_off;
+      sg.slot = it.slot;
+      sg.whole = chunk_count(r.kv_len, a.chunk_keys) == 1;
     }
+    fill_window(win, a, w0, 0, wcount);
   }
-  if (x0 >= x1) return;
-  __syncthreads();
-  for (; b < a.batch; ++b) {
-    const int cb = __builtin_amdgcn_readfirstlane(tab[6 * 64 + b]);
-    if (cb >= x1) break;
-    if (__builtin_amdgcn_readfirstlane(tab[7 * 64 + b]) == 0) continue;
-    r = make_req(__builtin_amdgcn_readfirstlane(tab[b]), __builtin_amdgcn_readfirstlane(tab[64 + b]),
-                 __builtin_amdgcn_readfirstlane(tab[128 + b]),
-                 __builtin_amdgcn_readfirstlane(tab[192 + b]),
-                 __builtin_amdgcn_readfirstlane(tab[256 + b]),
-                 __builtin_amdgcn_readfirstlane(tab[320 + b]), a.page_shift, a.num_kv_indices,
-                 a.tokens);
-    lo = max(x0 - cb, 0);
-    hi = min(x1 - cb, r.kv_len);
-    if (lo >= hi) continue;
-    // Opaque copies of the lane coordinates: what the segment derives from
-    // them is recomputed per segment instead of being hoisted out of this
-    // loop and held in registers across it.
-    int lane_s = lane, wave_s = wave, h_s = h;
-    asm volatile("" : "+v"(lane_s), "+v"(wave_s), "+s"(h_s));
-    process_segment<KV, D, RT, NS, ALT>(a, r, lo, hi, lo == 0 && hi == r.kv_len, blockIdx.x + b, h_s,
-                                        smem, wave_s, lane_s);
+  // Global stage numbering: inclusive prefix sum of the stage counts.
+  {
+    int incl = sg.nst;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int up = __shfl_up(incl, o);
+      if (lane >= o) incl += up;
+    }
+    sg.incl = incl;
+  }
+  const int nst_all = lane_val(sg.incl, 63);
+  // Segment holding global stage g (wave-uniform).
+  auto seg_of = [&](int g) { return (int)__popcll(__ballot(sg.incl <= g)); };
+  __syncthreads();  // page window written
+  if (nst_all == 0) return;
+
+  // ---- DMA issue of global stage g into ring buffer `buf`. Every wave runs
+  // this (a window move needs all of them); the DMA waves issue the loads.
+  const bool dma = DW == kSWaves || wave >= kSWaves - DW;
+  const int dw = DW == kSWaves ? wave : wave - (kSWaves - DW);
+  const bool uniform_pages = (1 << shift) >= G::KPI;
+  int wbase = 0;  // window index held in win[0]
+  auto issue = [&](int g, int buf) {
+    const int s = seg_of(g);
+    const int lo = lane_val(sg.lo, s), last = lane_val(sg.hi, s) - 1;
+    const int woff = lane_val(sg.woff, s);
+    const int n0 = lo + (g - (lane_val(sg.incl, s) - lane_val(sg.nst, s))) * kStageKeys;
+    if (woff + (min(n0 + kStageKeys - 1, last) >> shift) - wbase >= kStreamPageWindow) {
+      // Long work item: move the window (drains the ring; once per window).
+      wait_vmcnt<0>();
+      __syncthreads();
+      wbase = woff + (min(n0, last) >> shift);
+      fill_window(win, a, w0, wbase, wcount);
+      __syncthreads();
+    }
+    if (dma)
+      issue_stage<KV, D, DW>(a, win, wbase - woff, min(wcount - 1 - wbase, kStreamPageWindow - 1), h,
+                             n0, last, smem + buf * G::STAGE, dw, lane, uniform_pages);
+  };
+
+  // Computing wave w: row tile set w % waves_rows; with P = 2 the two waves
+  // of a tile set take the first and the second half of every stage's keys,
+  // and the second hands its softmax state to the first through LDS when a
+  // segment ends.
+  const int ncomp = a.waves_rows * P;
+  const bool computes = wave < ncomp;
+  const int tset = wave % a.waves_rows;
+  const int phase = wave / a.waves_rows;
+  const int row0 = tset * RT * 16;
+  float* pair_slot = (float*)(smem + NS * G::STAGE + kStreamPageWindow * 4) + tset * PairSlot<D, RT>::FLOATS;
+  RowSet<KV, D, RT> rs;
+  StreamAcc<D, RT> acc;
+  Vis vis{0, 0, a.has_mask};
+  bool has_rows = false;
+  int seg_L = 0;
+  auto start_segment = [&](int s) {
+    seg_L = lane_val(sg.L, s);
+    has_rows = row0 < a.group * seg_L;
+    rs.fetch(a, lane_val(sg.q_start, s), seg_L, lane_val(sg.mask_off, s), row0, h, lane);
+    vis.hi = lane_val(sg.hi, s);
+    vis.masked_from = lane_val(sg.prefix, s);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      acc.m[rt] = kNegInf;
+      acc.l[rt] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) acc.o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+
+  // ---- start-up: the first segment's rows are requested, then NS - 1
+  // stages (a short item repeats its last stage, so every DMA wave always
+  // issues the same number of loads here). The rows are older than every
+  // stage: waiting for all but the stages' loads leaves only the ring in
+  // flight.
+  if (computes) start_segment(seg_of(0));
+  for (int g = 0; g < NS - 1; ++g) issue(min(g, nst_all - 1), g);
+  if constexpr (DW == kSWaves) {
+    wait_vmcnt<(NS - 1) * G::NPW>();
+  } else {
+    if (computes) wait_vmcnt<0>();
+  }
+  if (computes) rs.finish(seg_L, a.has_mask);
+
+  // ---- the ring. Iteration g: DMA waves wait for their stage-g loads; the
+  // barrier (everyone's have landed and every wave is done with stage g - 1);
+  // the buffer of stage g - 1 is refilled with stage g + NS - 1; the
+  // computing waves take stage g (with P = 2 each wave of a pair takes half
+  // of its keys).
+  for (int g = 0; g < nst_all; ++g) {
+    if (dma) wait_stage<G::NPW, NS>(min(NS - 2, nst_all - 1 - g));
+    __builtin_amdgcn_s_barrier();
+    const int s = seg_of(g);
+    const int first = lane_val(sg.incl, s) - lane_val(sg.nst, s);
+    if (computes && g == first && g > 0) {
+      // A later segment: its rows are loaded here (before this iteration's
+      // DMA when the wave issues any) and waited for.
+      start_segment(s);
+      wait_vmcnt<0>();
+      rs.finish(seg_L, a.has_mask);
+    }
+    if (g + NS - 1 < nst_all) issue(g + NS - 1, (g + NS - 1) % NS);
+    if (computes && has_rows) {
+      const int n0 = lane_val(sg.lo, s) + (g - first) * kStageKeys;
+      const unsigned char* stage = smem + (g % NS) * G::STAGE;
+      compute_stage<KV, D, RT, kStageKeys / 16 / P>(acc, rs.qf, rs.row_t, rs.row_bits, vis, stage, n0,
+                                                    a.c_log2, lane, phase * (kStageKeys / 16 / P));
+    }
+    if (g == lane_val(sg.incl, s) - 1) {
+      // The segment's last stage (every wave sees it).
+      float lrow[RT];
+      if constexpr (P == 2) {
+        if (computes && has_rows && phase == 1) store_pair_state<D, RT>(acc, pair_slot, lane);
+        __syncthreads();
+        if (computes && has_rows && phase == 0) merge_pair_state<D, RT>(acc, lrow, pair_slot, true, lane);
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) lrow[rt] = rowsum4_v(acc.l[rt]);
+      }
+      if (computes && has_rows && phase == 0)
+        write_rows<KV, D, RT>(acc, lrow, rs, a, lane_val(sg.q_start, s), lane_val(sg.whole, s) != 0,
+                              lane_val(sg.slot, s), row0, h, lane);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-typedef void (*PartialFn)(PartialArgs);
-
+// `rt`: 16-row tiles per computing wave (1 or 2); `dma_waves`: 4 (the last
+// four waves issue the loads, the first ones compute) or 8; `pair`: 2 waves
+// per row tile set (each takes half of every stage's keys) or 1. Stage counts match the planner:
+// 128 KB of LDS / (2 * 64 * D * elem bytes), at most 8.
 template <int KV, int D, int NS>
-static PartialFn stream_rt(int tiles) {
-  switch (tiles) {
-    case 1: return vat_stream<KV, D, 1, NS, true>;
-    case 2: return vat_stream<KV, D, 1, NS, false>;
-    case 3:
-    case 4: return vat_stream<KV, D, 2, NS, false>;
-    default: return vat_stream<KV, D, 3, NS, false>;
-  }
+static const void* stream_variant(int rt, int dma_waves, int pair) {
+  if constexpr (KV != KV_E4M3)
+    if (rt == 2) return (const void*)vat_stream<KV, D, 2, NS, kSWaves, 1>;
+  if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1>;
+  return pair == 2 ? (const void*)vat_stream<KV, D, 1, NS, 4, 2> : (const void*)vat_stream<KV, D, 1, NS, 4, 1>;
 }
 
-// `tiles`: 16-row tiles of the row block (1..6). Stage counts match the
-// planner: 128 KB of LDS / (2 * 64 * D * elem bytes), at most 8.
-const void* stream_kernel(int kv_dtype, int head_dim, int tiles) {
+const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int pair) {
   if (kv_dtype == KV_BF16)
-    return (const void*)(head_dim == 128 ? stream_rt<KV_BF16, 128, 4>(tiles) : stream_rt<KV_BF16, 64, 8>(tiles));
-  return (const void*)stream_rt<KV_E4M3, 128, 8>(tiles);
+    return head_dim == 128 ? stream_variant<KV_BF16, 128, 4>(rt, dma_waves, pair)
+                           : stream_variant<KV_BF16, 64, 8>(rt, dma_waves, pair);
+  // The planner keeps fp8 at one row tile per wave.
+  return stream_variant<KV_E4M3, 128, 8>(1, dma_waves, pair);
 }
 
 }  // namespace vat

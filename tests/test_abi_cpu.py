@@ -140,30 +140,27 @@ def test_chunk_ids_of_consecutive_requests_are_disjoint():
                 used.add(cid)
 
 
-def slice_segments(kv_lens, qo_lens, slices, align=16):
-    """Host restatement of the balanced-slice layout: the (slice, request, lo,
-    hi, slot) segments the streaming kernel processes, and per request the
-    slots the merge reads (x_lo .. x_hi, slot x + b)."""
-    n = [(-(-k // align) * align) if (q > 0 and k > 0) else 0 for k, q in zip(kv_lens, qo_lens)]
-    cum = np.concatenate([[0], np.cumsum(n)]).astype(int)
-    total = int(cum[-1])
-    per = -(-(-(-total // slices)) // align) * align if total else 0
-    segs = []
-    for x in range(slices):
-        x0, x1 = x * per, min((x + 1) * per, total)
-        if x0 >= x1:
+def slice_segments(indptr, kv_lens, qo_lens, num_indices, slices, ps):
+    """Host restatement of the balanced-slice layout in page-index space: slice
+    x holds kv_indices positions [x per, (x + 1) per), per = ceil(num_indices /
+    slices); request b contributes keys [lo, hi) of the pages it has there.
+    Returns the (slice, request, lo, hi, slot) segments the streaming kernel
+    processes and, per request, the slots the merge reads (x_lo .. x_hi,
+    slot x + b)."""
+    per = -(-num_indices // slices)
+    segs, merged = [], {}
+    for b in range(len(kv_lens)):
+        p_start, p_end = int(indptr[b]), int(indptr[b + 1])
+        if qo_lens[b] == 0 or p_end == p_start:
             continue
-        for b in range(len(n)):
-            if cum[b] >= x1 or n[b] == 0:
-                continue
-            lo, hi = max(x0 - cum[b], 0), min(x1 - cum[b], kv_lens[b])
-            if lo < hi:
+        x_lo, x_hi = p_start // per, (p_end - 1) // per
+        merged[b] = [x + b for x in range(x_lo, x_hi + 1)]
+        for x in range(slices):
+            p0, p1 = max(p_start, x * per), min(p_end, min((x + 1) * per, num_indices))
+            if p0 < p1:
+                lo = (p0 - p_start) * ps
+                hi = min((p1 - p_start) * ps, kv_lens[b])
                 segs.append((x, b, lo, hi, x + b))
-    merged = {}
-    for b in range(len(n)):
-        if n[b]:
-            x_lo, x_hi = cum[b] // per, (cum[b] + kv_lens[b] - 1) // per
-            merged[b] = [x + b for x in range(x_lo, x_hi + 1)]
     return segs, merged
 
 
@@ -171,24 +168,29 @@ def test_slice_segments_cover_each_request_once():
     rng = np.random.default_rng(1)
     for _ in range(400):
         B = int(rng.integers(1, 65))
-        kv = rng.integers(0, 3000, size=B)
-        kv[rng.random(B) < 0.1] = 0
-        q = np.minimum(rng.integers(0, 9, size=B), kv)
+        ps = int(rng.choice([1, 4, 16, 64]))
+        pages = rng.integers(0, 200, size=B)
+        indptr = np.concatenate([[0], np.cumsum(pages)])
+        num_indices = int(indptr[-1]) + int(rng.integers(0, 4))
+        kv = [0 if n == 0 else (n - 1) * ps + int(rng.integers(1, ps + 1)) for n in pages]
+        q = [min(int(rng.integers(0, 9)), k) for k in kv]
         slices = int(rng.integers(1, 300))
-        segs, merged = slice_segments(list(kv), list(q), slices)
+        if num_indices == 0:
+            continue
+        segs, merged = slice_segments(indptr, kv, q, num_indices, slices, ps)
         slots = [s[4] for s in segs]
         assert len(set(slots)) == len(slots) and all(s < slices + B for s in slots)
         for b in range(B):
             mine = sorted((lo, hi, slot) for (_, bb, lo, hi, slot) in segs if bb == b)
             if q[b] == 0 or kv[b] == 0:
-                assert not mine
+                assert not mine and b not in merged
                 continue
             assert mine[0][0] == 0 and mine[-1][1] == kv[b]
+            assert all(lo < hi and lo % ps == 0 for lo, hi, _ in mine)
             assert all(mine[i][1] == mine[i + 1][0] for i in range(len(mine) - 1))
-            whole = len(mine) == 1
-            # The merge reads exactly the slots written as partials.
-            assert (merged[b] == [m[2] for m in mine]) or (whole and len(merged[b]) == 1)
-            assert all(lo % 16 == 0 for lo, _, _ in mine)
+            # The merge reads exactly the slots written as partials; a request
+            # inside one slice is written directly.
+            assert merged[b] == [m[2] for m in mine]
 
 
 @pytest.mark.parametrize("kw,code", [
