@@ -48,6 +48,22 @@ __device__ __forceinline__ void lds_wait_tied(s16x4& v) {
   static_assert(N >= 0 && N < 16, "lgkmcnt range");
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
 }
+// ds_read_b64_tr_b8, inline asm for the same reason. Within each 16-lane
+// group, output lane j receives byte j % 8 of the 8-byte chunks that source
+// lanes j / 8 + 2 k (k = 0..7) point at, as byte k.
+__device__ __forceinline__ u32x2 lds_read_tr8(const void* p) {
+  u32x2 v;
+  const unsigned addr = (unsigned)(uintptr_t)(const lds_void_t*)p;
+  asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+
+template <int N>
+__device__ __forceinline__ void lds_wait_tied(u32x2& v) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
+}
+
 template <int N>
 __device__ __forceinline__ void lds_wait_tied2(s16x4& v, s16x4& w) {
   static_assert(N >= 0 && N < 16, "lgkmcnt range");

@@ -293,27 +293,35 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
   };
   const unsigned char* vb = stage + G::BLK;
   if constexpr (KV == KV_E4M3) {
-    // Lane (d = l % 16, j = l / 16): codes of keys 16 kt + 4 j + e at d,
-    // decoded exactly to bf16.
-    auto vfrag = [&](int kt, int dt) {
-      const int kl0 = 16 * (kt0 + kt) + 4 * j4;
-      const int byte = 16 * dt + l16;
-      const int ch = byte >> 4, within = byte & 15;
-      unsigned b[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) b[e] = vb[(kl0 + e) * G::ROW + (swz<G::CPK>(kl0 + e, ch) << 4) + within];
-      const unsigned packed = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-      return __builtin_bit_cast(s16x4, u32x2{e4m3x2_to_bf16x2(packed, false), e4m3x2_to_bf16x2(packed, true)});
+    // One 8-bit transpose read per (32-key block, d tile): source lane s of
+    // the 16-lane group j points at the 8 codes of k index 8 j + s / 2 at
+    // d = 16 dt + 8 (s % 2) ..; lane (d, j) then receives the codes of k
+    // indices 8 j .. 8 j + 7 at d, decoded exactly to bf16 in registers.
+    constexpr int NB = KT / 2;
+    auto vaddr8 = [&](int kb, int dt) {
+      const int e = l16 >> 1;
+      const int kl = 16 * (kt0 + 2 * kb + (e >> 2)) + 4 * j4 + (e & 3);
+      return vb + kl * G::ROW + (swz<G::CPK>(kl, dt) << 4) + 8 * (l16 & 1);
     };
+    u32x2 raw[NB][NDT];
 #pragma unroll
-    for (int kb = 0; kb < KT / 2; ++kb)
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const s16x4 v0 = vfrag(2 * kb, dt), v1 = vfrag(2 * kb + 1, dt);
+      for (int dt = 0; dt < NDT; ++dt) raw[kb][dt] = lds_read_tr8(vaddr8(kb, dt));
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      ((lds_wait_tied<NB * NDT - 1 - I>(raw[I / NDT][I % NDT]),
+        [&] {
+          constexpr int kb = I / NDT, dt = I % NDT;
+          const bf16x8 va = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16(raw[kb][dt].x, raw[kb][dt].y));
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          acc.o[rt][dt] = mfma32(v0, v1, pb[2 * kb][rt], pb[2 * kb + 1][rt], acc.o[rt][dt]);
-      }
+          for (int rt = 0; rt < RT; ++rt) {
+            const u32x2 b0 = __builtin_bit_cast(u32x2, pb[2 * kb][rt]), b1 = __builtin_bit_cast(u32x2, pb[2 * kb + 1][rt]);
+            acc.o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                va, __builtin_bit_cast(bf16x8, u32x4{b0.x, b0.y, b1.x, b1.y}), acc.o[rt][dt], 0, 0, 0);
+          }
+        }()),
+       ...);
+    }(std::make_integer_sequence<int, NB * NDT>{});
   } else {
     // Transpose loads: source lane s of each 16-lane group points at the 8
     // bytes V[key 16 kt + 4 j + s / 4][d = 16 dt + 4 (s % 4) ..]; lane (d, j)
