@@ -70,6 +70,18 @@ __device__ __forceinline__ void lds_wait_tied2(s16x4& v, s16x4& w) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(v), "+v"(w) : "n"(N));
 }
 
+// Max / sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 // Max / sum over the four lanes l, l^16, l^32, l^48 that hold one query row.
 __device__ __forceinline__ float row_max4(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));

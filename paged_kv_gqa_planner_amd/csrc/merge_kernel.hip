@@ -4,7 +4,8 @@
 // w_i = 2^(lse_i - max lse), and the merged lse is max + log2(sum w).
 //
 // One wave per query row (each lane owns D / 64 head dims), four rows per
-// workgroup, partials combined online eight at a time. A request's partials
+// workgroup: the partials' lse give their max and weights, then the weighted
+// sum of their rows is formed. A request's partials
 // are its chunks (ids from chunk_start) or, with balanced slices of the
 // page-index space, the slices x_lo .. x_hi its pages fall in (slot x + b). Requests that fit one chunk or
 // slice were written directly by the partial kernel and are skipped.
@@ -53,44 +54,62 @@ __global__ __launch_bounds__(kMergeThreads) void vat_merge(MergeArgs a) {
     return (((long long)cid * a.hkv + h) * a.row_blocks + rb) * a.rows_per_block + local;
   };
 
-  // Online combination, eight chunks per round: their lse and output rows
-  // are all requested before any is used, so a request with up to eight
-  // chunks costs one round of loads.
-  constexpr int U = 8;
-  float m = kNegInf, den = 0.f;
+  // The first U partial rows are requested together with every partial's
+  // base-2 lse (lane i holds partials i, i + 64, ...), so a request with up
+  // to U partials costs one round of loads after its geometry.
+  constexpr int U = 16;
+  auto load_row = [&](int i, float (&v)[PER]) {
+    const float* po = a.part_o + slot(i) * D + lane * PER;
+    if constexpr (PER == 2) {
+      const float2 x2 = *(const float2*)po;
+      v[0] = x2.x;
+      v[1] = x2.y;
+    } else {
+      v[0] = po[0];
+    }
+  };
+  float v0[U][PER];
+#pragma unroll
+  for (int u = 0; u < U; ++u) load_row(min(u, n - 1), v0[u]);
+  const float ls0 = lane < n ? a.part_lse[slot(lane)] : kNegInf;
+  float m = ls0;
+  for (int i = lane + 64; i < n; i += 64) m = fmaxf(m, a.part_lse[slot(i)]);
+  m = wave_max(m);
+  const float mb = (m == kNegInf) ? 0.f : m;
+  // Weights w_i = 2^(lse_i - max) (0 for an empty partial) and the weighted
+  // sum of the rows; rows past the first U are requested U at a time.
+  float den = 0.f;
   float o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
-  for (int base = 0; base < n; base += U) {
-    float ls[U];
-    float v[U][PER];
+  for (int base = 0; base < n; base += 64) {
+    const int i = base + lane;
+    const float lsi = base == 0 ? ls0 : (i < n ? a.part_lse[slot(i)] : kNegInf);
+    const float w = fast_exp2(lsi - mb);
+    den += w;
+    const int cnt = min(64, n - base);
+    for (int j0 = 0; j0 < cnt; j0 += U) {
+      float v[U][PER], wj[U];
+      const bool first = base == 0 && j0 == 0;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool in = base + u < n;
-      const long long sl = slot(in ? base + u : 0);
-      ls[u] = in ? a.part_lse[sl] : kNegInf;
-      const float* po = a.part_o + sl * D + lane * PER;
-      if constexpr (PER == 2) {
-        const float2 x2 = in ? *(const float2*)po : float2{0.f, 0.f};
-        v[u][0] = x2.x;
-        v[u][1] = x2.y;
-      } else {
-        v[u][0] = in ? po[0] : 0.f;
+      for (int u = 0; u < U; ++u) {
+        const int j = min(j0 + u, cnt - 1);
+        wj[u] = j0 + u < cnt ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j))
+                             : 0.f;
+        if (first) {
+#pragma unroll
+          for (int k = 0; k < PER; ++k) v[u][k] = v0[u][k];
+        } else {
+          load_row(base + j, v[u]);
+        }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float m_new = fmaxf(m, ls[u]);
-      const float mb = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m - mb);  // 0 while m is -inf
-      const float w = fast_exp2(ls[u] - mb);  // 0 for an empty chunk
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int k = 0; k < PER; ++k) o[k] = o[k] * alpha + v[u][k] * w;
-      den = den * alpha + w;
-      m = m_new;
+        for (int k = 0; k < PER; ++k) o[k] += wj[u] * v[u][k];
     }
   }
-  const float mb = (m == kNegInf) ? 0.f : m;
+  den = wave_sum(den);
   const long long orow = (long long)(r.q_start + t) * a.hq + h * a.group + g;
   const float sc = den > 0.f ? a.v_scale / den : 0.f;
   if constexpr (QF32) {
