@@ -73,28 +73,28 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   const int64_t eb = elem_bytes(p->kv_dtype);
 
   // Kernel and row tiling.
-  //  * Streaming kernel (bf16 / fp8 caches, at most sixteen 16-row tiles per
-  //    KV head -- every verify shape): one row block; wave w of eight computes
-  //    row tiles [w rt, w rt + rt) over all keys (rt = 1 up to eight tiles,
-  //    else 2), so each key is read from HBM once and no two waves share a
-  //    row's softmax state.
-  //  * Row-tiled kernel (fp32 caches, wider row sets such as prefill): a wave
-  //    holds RT tiles; waves split the rows and, when rows are few, the keys.
+  //  * Streaming kernel (bf16 / fp8 caches): wave w of eight computes row
+  //    tiles [w rt, w rt + rt) of a row block over all of the block's keys
+  //    (rt = 1 up to eight tiles, else 2: blocks of 128 or 256 rows), so each
+  //    key is read from HBM once per row block and no two waves share a row's
+  //    softmax state. Verify shapes fit one block; a prefill takes several.
+  //  * Row-tiled kernel (fp32 caches, fp8 with D = 64): a wave holds RT
+  //    tiles; waves split the rows and, when rows are few, the keys.
   int rt, wr, wk;
   // fp8 caches with D = 64 have too few 1 KB loads per stage for eight waves;
   // with fp8 the decode registers leave room for one row tile per wave.
   const bool fp8 = p->kv_dtype == VAT_FP8_E4M3FN;
-  const bool stream = (p->kv_dtype != VAT_F32) &&
-                      tiles <= (fp8 ? kStreamThreads / 64 : kStreamMaxTiles) &&
-                      !(fp8 && p->head_dim == 64);
+  const bool stream = (p->kv_dtype != VAT_F32) && !(fp8 && p->head_dim == 64);
   int dw = 0;
   if (stream) {
-    rt = tiles <= kStreamThreads / 64 ? 1 : 2;
-    wr = int(cdiv(tiles, rt));
+    const int64_t max_tiles = fp8 ? kStreamThreads / 64 : kStreamMaxTiles;
+    const int64_t bt = tiles <= max_tiles ? tiles : max_tiles;  // tiles per row block
+    rt = bt <= kStreamThreads / 64 ? 1 : 2;
+    wr = int(cdiv(bt, rt));
     // One or two row tiles: two waves per tile split every stage's keys
     // (their softmax states meet in LDS at the end of each segment), so four
     // SIMDs share the math.
-    wk = tiles <= 2 ? 2 : 1;
+    wk = bt <= 2 ? 2 : 1;
     // Up to four computing waves leave the last four to issue the DMA alone,
     // so a computing wave never stalls behind the memory queue.
     dw = wr * wk <= 4 ? 4 : kStreamThreads / 64;
@@ -165,7 +165,8 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
     ck = whole;
   } else if (p->chunk_keys > 0) {
     ck = p->chunk_keys;
-  } else if (!stream && base_items >= 4 * int64_t(num_cus)) {
+  } else if (base_items >= 4 * int64_t(num_cus) || (stream && RB > 1 && base_items >= int64_t(num_cus))) {
+    // Enough (request, KV head, row block) items to fill the chip.
     ck = whole;
   } else if (stream) {
     // Split the average request evenly into as many chunks as leave one
@@ -186,7 +187,7 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   if (ck > int64_t(INT32_MAX) / 2) return VAT_ERR_UNSUPPORTED;
   // Balanced key slices (streaming kernel, planner's choice, small batches):
   // one workgroup per CU share of each KV head, whatever the length mix.
-  if (stream && p->chunk_keys == -1 && p->batch <= kSliceMaxBatch) {
+  if (stream && RB == 1 && p->chunk_keys == -1 && p->batch <= kSliceMaxBatch) {
     int64_t nx = int64_t(num_cus) / p->num_kv_heads;
     if (nx < 1) nx = 1;
     plan->slices = int32_t(nx);

@@ -164,6 +164,7 @@ struct Vis {
   int hi;           // keys >= hi are outside the item
   int masked_from;  // keys >= masked_from are drafts: causal or mask
   int has_mask;
+  int t_min;        // smallest query token among this wave's rows
 };
 
 // An empty volatile asm statement: the rare branch it sits in (masking of the
@@ -223,7 +224,12 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
   }
   // ---- keys past the item, drafts under causal / mask. Lane (row, j) holds
   // keys 16 kt + 4 j + e.
-  if (n0 + kStageKeys > vis.hi || n0 + kStageKeys > vis.masked_from) {
+  // Only stages that reach past the item, or hold drafts some row of this
+  // wave may not see, test keys one by one (a causal stage whose drafts all
+  // precede every row's token is fully visible).
+  const int n_last = n0 + kStageKeys - 1;
+  if (n_last >= vis.hi ||
+      (n_last >= vis.masked_from && (vis.has_mask || n_last - vis.masked_from > vis.t_min))) {
     keep_branch();
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
@@ -465,14 +471,15 @@ struct RowSet {
 // out (bf16) and natural-log lse for a whole request, otherwise a normalised
 // fp32 partial (v_scale not yet applied) and its base-2 log-sum-exp in slot
 // `slot`.
+// `rb`: row block; `row0`: this wave's first row within the block.
 template <int KV, int D, int RT>
 __device__ __forceinline__ void write_rows(const StreamAcc<D, RT>& acc, const float (&lrow)[RT],
                                            const RowSet<KV, D, RT>& rs, const PartialArgs& a,
-                                           int q_start, bool whole, int slot, int row0, int h,
-                                           int lane) {
+                                           int q_start, bool whole, int slot, int rb, int row0,
+                                           int h, int lane) {
   constexpr int NDT = D / 16;
   const int l16 = lane & 15, j4 = lane >> 4;
-  const long long pid = (long long)slot * a.hkv + h;
+  const long long pid = ((long long)slot * a.hkv + h) * a.row_blocks + rb;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const float lsum = lrow[rt];
@@ -567,7 +574,10 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   int* win = (int*)(smem + NS * G::STAGE);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int h = blockIdx.y;
+  // Row blocks of one KV head are dispatched longest first (under a causal
+  // limit a later block reaches more keys).
+  const int h = blockIdx.y / a.row_blocks;
+  const int rb = a.row_blocks - 1 - (int)(blockIdx.y % a.row_blocks);
   const int shift = a.page_shift;
 
   // ---- the segment lanes and the page window: one round of loads for a slice
@@ -617,8 +627,15 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
     Req r;
     Item it;
     if (!find_item(ra, blockIdx.x, lane, r, it) || r.L == 0) return;
+    if (rb * a.rows_per_block >= a.group * r.L) return;  // no row of this block exists
     const int lo = it.j * a.chunk_keys;
-    const int hi = min(lo + a.chunk_keys, r.kv_len);
+    int hi = min(lo + a.chunk_keys, r.kv_len);
+    const bool whole_item = chunk_count(r.kv_len, a.chunk_keys) == 1;
+    if (whole_item && !a.has_mask) {
+      // Causal: no row of this block sees a key past its last row's token.
+      const int t_hi = min(r.L - 1, (rb * a.rows_per_block + a.rows_per_block - 1) / a.group);
+      hi = min(hi, r.prefix + t_hi + 1);
+    }
     if (lo >= hi) return;
     w0 = r.kv_start + (lo >> shift);
     wcount = ((hi - 1) >> shift) - (lo >> shift) + 1;
@@ -632,7 +649,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
       sg.prefix = r.prefix;
       sg.mask_off = r.mask_off;
       sg.slot = it.slot;
-      sg.whole = chunk_count(r.kv_len, a.chunk_keys) == 1;
+      sg.whole = whole_item;
     }
     fill_window(win, a, w0, 0, wcount);
   }
@@ -684,19 +701,21 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   const bool computes = wave < ncomp;
   const int tset = wave % a.waves_rows;
   const int phase = wave / a.waves_rows;
-  const int row0 = tset * RT * 16;
+  const int row0 = tset * RT * 16;                  // within the row block
+  const int rbase = rb * a.rows_per_block + row0;   // in the request's rows
   float* pair_slot = (float*)(smem + NS * G::STAGE + kStreamPageWindow * 4) + tset * PairSlot<D, RT>::FLOATS;
   RowSet<KV, D, RT> rs;
   StreamAcc<D, RT> acc;
-  Vis vis{0, 0, a.has_mask};
+  Vis vis{0, 0, a.has_mask, 0};
   bool has_rows = false;
   int seg_L = 0;
   auto start_segment = [&](int s) {
     seg_L = lane_val(sg.L, s);
-    has_rows = row0 < a.group * seg_L;
-    rs.fetch(a, lane_val(sg.q_start, s), seg_L, lane_val(sg.mask_off, s), row0, h, lane);
+    has_rows = rbase < a.group * seg_L;
+    rs.fetch(a, lane_val(sg.q_start, s), seg_L, lane_val(sg.mask_off, s), rbase, h, lane);
     vis.hi = lane_val(sg.hi, s);
     vis.masked_from = lane_val(sg.prefix, s);
+    vis.t_min = rbase / a.group;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       acc.m[rt] = kNegInf;
@@ -758,7 +777,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
       }
       if (computes && has_rows && phase == 0)
         write_rows<KV, D, RT>(acc, lrow, rs, a, lane_val(sg.q_start, s), lane_val(sg.whole, s) != 0,
-                              lane_val(sg.slot, s), row0, h, lane);
+                              lane_val(sg.slot, s), rb, row0, h, lane);
     }
   }
 }

@@ -92,7 +92,9 @@ def test_plans_for_the_workloads(lib, cid):
     if cid == 1:
         assert plan.kernel == 0 and plan.slices == 0  # fp32 caches take the row-tiled kernel
     elif cid == 4:
-        assert plan.kernel == 0 and plan.direct == 1 and plan.workspace_bytes == 0
+        # Prefill: the streaming kernel in row blocks of 256 rows, whole requests.
+        assert plan.kernel == 1 and plan.direct == 1 and plan.workspace_bytes == 0
+        assert plan.rows_per_block == 256 and plan.row_blocks == 32 and plan.slices == 0
     else:
         assert plan.kernel == 1 and plan.threads == 512 and plan.slices > 0
     if not plan.direct:
