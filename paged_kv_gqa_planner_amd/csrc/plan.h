@@ -18,6 +18,11 @@ constexpr int kStepKeys = 32;
 // ring may fill.
 constexpr int kStreamThreads = 512;
 constexpr int kStageKeys = 64;
+// Keys per streaming stage: 64 when a key row is 256 bytes (bf16, D = 128),
+// else 128, so a stage is 32 KB either way.
+constexpr int stream_stage_keys(int kv_dtype, int head_dim) {
+  return (kv_dtype == VAT_BF16 && head_dim == 128) ? 64 : 128;
+}
 constexpr int kStreamMaxTiles = 16;
 constexpr int kStreamLdsBudget = 128 * 1024;
 // Page ids the streaming kernel keeps in LDS at a time.

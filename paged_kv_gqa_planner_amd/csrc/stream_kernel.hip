@@ -35,17 +35,18 @@ namespace vat {
 
 constexpr int kSWaves = kStreamThreads / 64;  // 8
 
-// DW: waves issuing the DMA (4: the last four of eight; 8: all of them).
-template <int KV, int D, int DW = kSWaves>
+// DW: waves issuing the DMA (4: the last four of eight; 8: all of them);
+// SK: keys per stage.
+template <int KV, int D, int DW = kSWaves, int SK = kStageKeys>
 struct StreamGeom {
   static constexpr int EB = (KV == KV_E4M3) ? 1 : 2;  // bytes per cache element
   static constexpr int ROW = D * EB;                   // bytes per key row
   static constexpr int CPK = ROW / 16;                 // 16-byte chunks per key row
   static constexpr int KPI = 64 / CPK;                 // keys per 1 KB DMA instruction
-  static constexpr int NINST = kStageKeys / KPI;       // DMA instructions per K (or V) block
+  static constexpr int NINST = SK / KPI;               // DMA instructions per K (or V) block
   static constexpr int IPW = NINST / DW;               // per DMA wave per block
   static constexpr int NPW = 2 * IPW;                  // per DMA wave per stage (K and V)
-  static constexpr int BLK = kStageKeys * ROW;         // bytes of one K (or V) block
+  static constexpr int BLK = SK * ROW;                 // bytes of one K (or V) block
   static constexpr int STAGE = 2 * BLK;
   static_assert(IPW >= 1 && NINST % DW == 0, "stage must split over the DMA waves");
 };
@@ -89,12 +90,12 @@ __device__ __forceinline__ unsigned cvt_pk_bf16(float lo, float hi) {
 // Issue this wave's share of the DMA loads of one stage: keys n0 .. n0 + 63,
 // each clamped to `last` (the item's last key) so every address is a real
 // cached entry; keys past the item are masked out of the softmax later.
-template <int KV, int D, int DW>
+template <int KV, int D, int DW, int SK>
 __device__ __forceinline__ void issue_stage(const PartialArgs& a, const int* win, int win_base,
                                             int last_rel, int h, int n0, int last,
                                             unsigned char* stage, int dw, int lane,
                                             bool uniform_pages) {
-  using G = StreamGeom<KV, D, DW>;
+  using G = StreamGeom<KV, D, DW, SK>;
   const int ps_mask = (1 << a.page_shift) - 1;
   const long long page_bytes = (long long)G::ROW * a.hkv << a.page_shift;
   int pg[G::IPW];
@@ -176,15 +177,16 @@ __device__ __forceinline__ void keep_branch() { asm volatile(""); }
 // are processed together: their S^T MFMAs interleave, the softmax takes one
 // row max over all 64 keys, and the V^T reads of tile kt + 1 are in flight
 // while tile kt's PV MFMAs run.
-// KT: 16-key tiles this wave takes, tiles kt0 .. kt0 + KT - 1 of the stage.
-template <int KV, int D, int RT, int KT>
+// KT: 16-key tiles this wave takes, tiles kt0 .. kt0 + KT - 1 of an SK-key
+// stage.
+template <int KV, int D, int RT, int KT, int SK = kStageKeys>
 __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsigned (&qf)[RT][D / 8],
                                               const int (&row_t)[RT],
                                               const unsigned long long (&row_bits)[RT],
                                               const Vis& vis, const unsigned char* stage, int n0,
                                               float c, int lane, int kt0) {
-  using G = StreamGeom<KV, D>;
-  static_assert(KT == 2 || KT == 4, "one or two 32-key blocks");
+  using G = StreamGeom<KV, D, kSWaves, SK>;
+  static_assert(KT == 2 || KT == 4 || KT == 8, "one to four 32-key blocks");
   constexpr int NDT = D / 16;
   const int l16 = lane & 15;
   const int j4 = lane >> 4;
@@ -227,7 +229,7 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
   // Only stages that reach past the item, or hold drafts some row of this
   // wave may not see, test keys one by one (a causal stage whose drafts all
   // precede every row's token is fully visible).
-  const int n_last = n0 + kStageKeys - 1;
+  const int n_last = n0 + SK - 1;
   if (n_last >= vis.hi ||
       (n_last >= vis.masked_from && (vis.has_mask || n_last - vis.masked_from > vis.t_min))) {
     keep_branch();
@@ -298,83 +300,92 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
                                                    c, 0, 0, 0);
   };
   const unsigned char* vb = stage + G::BLK;
+  constexpr int NB = KT / 2;  // 32-key blocks
   if constexpr (KV == KV_E4M3) {
     // One 8-bit transpose read per (32-key block, d tile): source lane s of
     // the 16-lane group j points at the 8 codes of k index 8 j + s / 2 at
     // d = 16 dt + 8 (s % 2) ..; lane (d, j) then receives the codes of k
     // indices 8 j .. 8 j + 7 at d, decoded exactly to bf16 in registers.
-    constexpr int NB = KT / 2;
+    // Block kb + 1's reads are in flight while block kb's MFMAs run.
     auto vaddr8 = [&](int kb, int dt) {
       const int e = l16 >> 1;
       const int kl = 16 * (kt0 + 2 * kb + (e >> 2)) + 4 * j4 + (e & 3);
       return vb + kl * G::ROW + (swz<G::CPK>(kl, dt) << 4) + 8 * (l16 & 1);
     };
-    u32x2 raw[NB][NDT];
+    u32x2 raw[2][NDT];
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
+    for (int dt = 0; dt < NDT; ++dt) raw[0][dt] = lds_read_tr8(vaddr8(0, dt));
+    [&]<int... K>(std::integer_sequence<int, K...>) {
+      (
+          [&] {
+            constexpr int kb = K;
+            constexpr bool more = kb + 1 < NB;
+            if constexpr (more) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) raw[kb][dt] = lds_read_tr8(vaddr8(kb, dt));
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-      ((lds_wait_tied<NB * NDT - 1 - I>(raw[I / NDT][I % NDT]),
-        [&] {
-          constexpr int kb = I / NDT, dt = I % NDT;
-          const bf16x8 va = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16(raw[kb][dt].x, raw[kb][dt].y));
+              for (int dt = 0; dt < NDT; ++dt) raw[(kb + 1) & 1][dt] = lds_read_tr8(vaddr8(kb + 1, dt));
+            }
+            [&]<int... I>(std::integer_sequence<int, I...>) {
+              ((lds_wait_tied<(more ? NDT : 0) + NDT - 1 - I>(raw[kb & 1][I]),
+                [&] {
+                  const bf16x8 va = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16(raw[kb & 1][I].x, raw[kb & 1][I].y));
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            const u32x2 b0 = __builtin_bit_cast(u32x2, pb[2 * kb][rt]), b1 = __builtin_bit_cast(u32x2, pb[2 * kb + 1][rt]);
-            acc.o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                va, __builtin_bit_cast(bf16x8, u32x4{b0.x, b0.y, b1.x, b1.y}), acc.o[rt][dt], 0, 0, 0);
-          }
-        }()),
-       ...);
-    }(std::make_integer_sequence<int, NB * NDT>{});
+                  for (int rt = 0; rt < RT; ++rt) {
+                    const u32x2 b0 = __builtin_bit_cast(u32x2, pb[2 * kb][rt]);
+                    const u32x2 b1 = __builtin_bit_cast(u32x2, pb[2 * kb + 1][rt]);
+                    acc.o[rt][I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        va, __builtin_bit_cast(bf16x8, u32x4{b0.x, b0.y, b1.x, b1.y}), acc.o[rt][I], 0, 0, 0);
+                  }
+                }()),
+               ...);
+            }(std::make_integer_sequence<int, NDT>{});
+          }(),
+          ...);
+    }(std::make_integer_sequence<int, NB>{});
   } else {
     // Transpose loads: source lane s of each 16-lane group points at the 8
     // bytes V[key 16 kt + 4 j + s / 4][d = 16 dt + 4 (s % 4) ..]; lane (d, j)
-    // then receives V[16 kt + 4 j + e][16 dt + d], e = 0..3. Each MFMA waits
-    // only for its own reads (LDS reads complete in order).
+    // then receives V[16 kt + 4 j + e][16 dt + d], e = 0..3. Block kb's
+    // second tile, and with one row tile block kb + 1's first, are requested
+    // before block kb's MFMAs; each MFMA waits only for its own reads (LDS
+    // reads complete in order).
     const int klb = 4 * j4 + (l16 >> 2);
     auto vaddr = [&](int kt, int dt) {
       const int kl = 16 * (kt0 + kt) + klb;
       const int d0 = 16 * dt + 4 * (l16 & 3);
       return vb + kl * G::ROW + (swz<G::CPK>(kl, d0 >> 3) << 4) + (d0 & 7) * 2;
     };
-    s16x4 v0[NDT], v1[NDT], v2[NDT], v3[NDT];
+    constexpr bool kAhead = RT == 1;  // registers for a third tile of reads
+    constexpr int NBUF = kAhead ? 2 : 1;
+    s16x4 va[NBUF][NDT], vv[NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) v0[dt] = lds_read_tr16(vaddr(0, dt));
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) v1[dt] = lds_read_tr16(vaddr(1, dt));
-    // With two blocks and one row tile the third tile's reads go out before
-    // the first block's MFMAs.
-    constexpr bool kAhead = KT == 4 && RT == 1;
-    if constexpr (kAhead) {
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) v2[dt] = lds_read_tr16(vaddr(2, dt));
-    }
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-      ((lds_wait_tied2<(kAhead ? NDT : 0) + NDT - 1 - I>(v0[I], v1[I]),
-        [&] {
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) acc.o[rt][I] = mfma32(v0[I], v1[I], pb[0][rt], pb[1][rt], acc.o[rt][I]);
-        }()),
-       ...);
-    }(std::make_integer_sequence<int, NDT>{});
-    if constexpr (KT == 4) {
-      if constexpr (!kAhead) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) v2[dt] = lds_read_tr16(vaddr(2, dt));
-      }
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) v3[dt] = lds_read_tr16(vaddr(3, dt));
-      [&]<int... I>(std::integer_sequence<int, I...>) {
-        ((lds_wait_tied2<NDT - 1 - I>(v2[I], v3[I]),
+    for (int dt = 0; dt < NDT; ++dt) va[0][dt] = lds_read_tr16(vaddr(0, dt));
+    [&]<int... K>(std::integer_sequence<int, K...>) {
+      (
           [&] {
+            constexpr int kb = K;
+            constexpr bool ahead = kAhead && kb + 1 < NB;
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) acc.o[rt][I] = mfma32(v2[I], v3[I], pb[2][rt], pb[3][rt], acc.o[rt][I]);
-          }()),
-         ...);
-      }(std::make_integer_sequence<int, NDT>{});
-    }
+            for (int dt = 0; dt < NDT; ++dt) vv[dt] = lds_read_tr16(vaddr(2 * kb + 1, dt));
+            if constexpr (ahead) {
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt) va[(kb + 1) % NBUF][dt] = lds_read_tr16(vaddr(2 * kb + 2, dt));
+            }
+            [&]<int... I>(std::integer_sequence<int, I...>) {
+              ((lds_wait_tied2<(ahead ? NDT : 0) + NDT - 1 - I>(va[kb % NBUF][I], vv[I]),
+                [&] {
+#pragma unroll
+                  for (int rt = 0; rt < RT; ++rt)
+                    acc.o[rt][I] = mfma32(va[kb % NBUF][I], vv[I], pb[2 * kb][rt], pb[2 * kb + 1][rt], acc.o[rt][I]);
+                }()),
+               ...);
+            }(std::make_integer_sequence<int, NDT>{});
+            if constexpr (!kAhead && kb + 1 < NB) {
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt) va[(kb + 1) % NBUF][dt] = lds_read_tr16(vaddr(2 * kb + 2, dt));
+            }
+          }(),
+          ...);
+    }(std::make_integer_sequence<int, NB>{});
   }
 }
 
@@ -567,9 +578,9 @@ __device__ __forceinline__ void merge_pair_state(StreamAcc<D, RT>& acc, float (&
 // through one ring of LDS buffers filled by DMA. Wave w < waves_rows owns row
 // tiles [w RT, w RT + RT) of every segment and runs all of its keys, so no
 // two waves ever hold parts of the same row; all eight waves issue the DMA.
-template <int KV, int D, int RT, int NS, int DW, int P>
+template <int KV, int D, int RT, int NS, int DW, int P, int SK>
 __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
-  using G = StreamGeom<KV, D, DW>;
+  using G = StreamGeom<KV, D, DW, SK>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   int* win = (int*)(smem + NS * G::STAGE);
   const int lane = threadIdx.x & 63;
@@ -606,7 +617,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
     if (in && r.L > 0 && p0 < p1) {
       sg.lo = (p0 - r.kv_start) << shift;
       sg.hi = min((p1 - r.kv_start) << shift, r.kv_len);
-      sg.nst = (sg.hi - sg.lo + kStageKeys - 1) / kStageKeys;
+      sg.nst = (sg.hi - sg.lo + SK - 1) / SK;
       sg.woff = r.kv_start - w0;
       sg.q_start = r.q_start;
       sg.L = r.L;
@@ -642,7 +653,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
     if (lane == 0) {
       sg.lo = lo;
       sg.hi = hi;
-      sg.nst = (hi - lo + kStageKeys - 1) / kStageKeys;
+      sg.nst = (hi - lo + SK - 1) / SK;
       sg.woff = r.kv_start - w0;
       sg.q_start = r.q_start;
       sg.L = r.L;
@@ -679,8 +690,8 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
     const int s = seg_of(g);
     const int lo = lane_val(sg.lo, s), last = lane_val(sg.hi, s) - 1;
     const int woff = lane_val(sg.woff, s);
-    const int n0 = lo + (g - (lane_val(sg.incl, s) - lane_val(sg.nst, s))) * kStageKeys;
-    if (woff + (min(n0 + kStageKeys - 1, last) >> shift) - wbase >= kStreamPageWindow) {
+    const int n0 = lo + (g - (lane_val(sg.incl, s) - lane_val(sg.nst, s))) * SK;
+    if (woff + (min(n0 + SK - 1, last) >> shift) - wbase >= kStreamPageWindow) {
       // Long work item: move the window (drains the ring; once per window).
       wait_vmcnt<0>();
       __syncthreads();
@@ -689,7 +700,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
       __syncthreads();
     }
     if (dma)
-      issue_stage<KV, D, DW>(a, win, wbase - woff, min(wcount - 1 - wbase, kStreamPageWindow - 1), h,
+      issue_stage<KV, D, DW, SK>(a, win, wbase - woff, min(wcount - 1 - wbase, kStreamPageWindow - 1), h,
                              n0, last, smem + buf * G::STAGE, dw, lane, uniform_pages);
   };
 
@@ -759,10 +770,10 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
     }
     if (g + NS - 1 < nst_all) issue(g + NS - 1, (g + NS - 1) % NS);
     if (computes && has_rows) {
-      const int n0 = lane_val(sg.lo, s) + (g - first) * kStageKeys;
+      const int n0 = lane_val(sg.lo, s) + (g - first) * SK;
       const unsigned char* stage = smem + (g % NS) * G::STAGE;
-      compute_stage<KV, D, RT, kStageKeys / 16 / P>(acc, rs.qf, rs.row_t, rs.row_bits, vis, stage, n0,
-                                                    a.c_log2, lane, phase * (kStageKeys / 16 / P));
+      compute_stage<KV, D, RT, SK / 16 / P, SK>(acc, rs.qf, rs.row_t, rs.row_bits, vis, stage, n0,
+                                                a.c_log2, lane, phase * (SK / 16 / P));
     }
     if (g == lane_val(sg.incl, s) - 1) {
       // The segment's last stage (every wave sees it).
@@ -785,22 +796,25 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
 // ---------------------------------------------------------------------------
 // `rt`: 16-row tiles per computing wave (1 or 2); `dma_waves`: 4 (the last
 // four waves issue the loads, the first ones compute) or 8; `pair`: 2 waves
-// per row tile set (each takes half of every stage's keys) or 1. Stage counts match the planner:
-// 128 KB of LDS / (2 * 64 * D * elem bytes), at most 8.
-template <int KV, int D, int NS>
+// per row tile set (each takes half of every stage's keys) or 1. Stages hold
+// 32 KB (64 bf16 keys of D = 128, else 128 keys); four of them fill the
+// 128 KB the planner gives the ring.
+template <int KV, int D, int NS, int SK>
 static const void* stream_variant(int rt, int dma_waves, int pair) {
   if constexpr (KV != KV_E4M3)
-    if (rt == 2) return (const void*)vat_stream<KV, D, 2, NS, kSWaves, 1>;
-  if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1>;
-  return pair == 2 ? (const void*)vat_stream<KV, D, 1, NS, 4, 2> : (const void*)vat_stream<KV, D, 1, NS, 4, 1>;
+    if (rt == 2) return (const void*)vat_stream<KV, D, 2, NS, kSWaves, 1, SK>;
+  if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK>;
+  return pair == 2 ? (const void*)vat_stream<KV, D, 1, NS, 4, 2, SK> : (const void*)vat_stream<KV, D, 1, NS, 4, 1, SK>;
 }
 
 const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int pair) {
+  static_assert(stream_stage_keys(KV_BF16, 128) == 64 && stream_stage_keys(KV_BF16, 64) == 128 &&
+                stream_stage_keys(KV_E4M3, 128) == 128, "stage sizes match the planner");
   if (kv_dtype == KV_BF16)
-    return head_dim == 128 ? stream_variant<KV_BF16, 128, 4>(rt, dma_waves, pair)
-                           : stream_variant<KV_BF16, 64, 8>(rt, dma_waves, pair);
+    return head_dim == 128 ? stream_variant<KV_BF16, 128, 4, 64>(rt, dma_waves, pair)
+                           : stream_variant<KV_BF16, 64, 4, 128>(rt, dma_waves, pair);
   // The planner keeps fp8 at one row tile per wave.
-  return stream_variant<KV_E4M3, 128, 8>(1, dma_waves, pair);
+  return stream_variant<KV_E4M3, 128, 4, 128>(1, dma_waves, pair);
 }
 
 }  // namespace vat
