@@ -95,9 +95,9 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
     // (their softmax states meet in LDS at the end of each segment), so four
     // SIMDs share the math.
     wk = bt <= 2 ? 2 : 1;
-    // Up to four computing waves leave the last four to issue the DMA alone,
-    // so a computing wave never stalls behind the memory queue.
-    dw = wr * wk <= 4 ? 4 : kStreamThreads / 64;
+    // Up to six computing waves leave the last four (or two) to issue the DMA
+    // alone, so a computing wave never stalls behind the memory queue.
+    dw = wr * wk <= 4 ? 4 : (rt == 1 && wr * wk <= 6 ? 2 : kStreamThreads / 64);
   } else if (tiles <= 3) {
     rt = int(tiles);
     wr = 1;

@@ -35,7 +35,7 @@ namespace vat {
 
 constexpr int kSWaves = kStreamThreads / 64;  // 8
 
-// DW: waves issuing the DMA (4: the last four of eight; 8: all of them);
+// DW: waves issuing the DMA (2 or 4: the last ones of eight; 8: all of them);
 // SK: keys per stage.
 template <int KV, int D, int DW = kSWaves, int SK = kStageKeys>
 struct StreamGeom {
@@ -794,8 +794,8 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// `rt`: 16-row tiles per computing wave (1 or 2); `dma_waves`: 4 (the last
-// four waves issue the loads, the first ones compute) or 8; `pair`: 2 waves
+// `rt`: 16-row tiles per computing wave (1 or 2); `dma_waves`: 2 or 4 (the
+// last waves issue the loads, the first ones compute) or 8 (all issue); `pair`: 2 waves
 // per row tile set (each takes half of every stage's keys) or 1. Stages hold
 // 32 KB (64 bf16 keys of D = 128, else 128 keys); four of them fill the
 // 128 KB the planner gives the ring.
@@ -804,6 +804,7 @@ static const void* stream_variant(int rt, int dma_waves, int pair) {
   if constexpr (KV != KV_E4M3)
     if (rt == 2) return (const void*)vat_stream<KV, D, 2, NS, kSWaves, 1, SK>;
   if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK>;
+  if (dma_waves == 2) return (const void*)vat_stream<KV, D, 1, NS, 2, 1, SK>;
   return pair == 2 ? (const void*)vat_stream<KV, D, 1, NS, 4, 2, SK> : (const void*)vat_stream<KV, D, 1, NS, 4, 1, SK>;
 }
 
