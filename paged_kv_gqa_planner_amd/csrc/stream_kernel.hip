@@ -662,7 +662,6 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
       sg.slot = it.slot;
       sg.whole = whole_item;
     }
-    fill_window(win, a, w0, 0, wcount);
   }
   // Global stage numbering: inclusive prefix sum of the stage counts.
   {
@@ -677,32 +676,6 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   const int nst_all = lane_val(sg.incl, 63);
   // Segment holding global stage g (wave-uniform).
   auto seg_of = [&](int g) { return (int)__popcll(__ballot(sg.incl <= g)); };
-  __syncthreads();  // page window written
-  if (nst_all == 0) return;
-
-  // ---- DMA issue of global stage g into ring buffer `buf`. Every wave runs
-  // this (a window move needs all of them); the DMA waves issue the loads.
-  const bool dma = DW == kSWaves || wave >= kSWaves - DW;
-  const int dw = DW == kSWaves ? wave : wave - (kSWaves - DW);
-  const bool uniform_pages = (1 << shift) >= G::KPI;
-  int wbase = 0;  // window index held in win[0]
-  auto issue = [&](int g, int buf) {
-    const int s = seg_of(g);
-    const int lo = lane_val(sg.lo, s), last = lane_val(sg.hi, s) - 1;
-    const int woff = lane_val(sg.woff, s);
-    const int n0 = lo + (g - (lane_val(sg.incl, s) - lane_val(sg.nst, s))) * SK;
-    if (woff + (min(n0 + SK - 1, last) >> shift) - wbase >= kStreamPageWindow) {
-      // Long work item: move the window (drains the ring; once per window).
-      wait_vmcnt<0>();
-      __syncthreads();
-      wbase = woff + (min(n0, last) >> shift);
-      fill_window(win, a, w0, wbase, wcount);
-      __syncthreads();
-    }
-    if (dma)
-      issue_stage<KV, D, DW, SK>(a, win, wbase - woff, min(wcount - 1 - wbase, kStreamPageWindow - 1), h,
-                             n0, last, smem + buf * G::STAGE, dw, lane, uniform_pages);
-  };
 
   // Computing wave w: row tile set w % waves_rows; with P = 2 the two waves
   // of a tile set take the first and the second half of every stage's keys,
@@ -737,12 +710,41 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   };
 
 
-  // ---- start-up: the first segment's rows are requested, then NS - 1
-  // stages (a short item repeats its last stage, so every DMA wave always
-  // issues the same number of loads here). The rows are older than every
-  // stage: waiting for all but the stages' loads leaves only the ring in
-  // flight.
-  if (computes) start_segment(seg_of(0));
+  // The first segment's rows are requested now, in flight together with a
+  // chunk's page ids.
+  if (computes && nst_all > 0) start_segment(seg_of(0));
+  if (a.slices == 0) fill_window(win, a, w0, 0, wcount);
+  __syncthreads();  // page window written
+  if (nst_all == 0) return;
+
+  // ---- DMA issue of global stage g into ring buffer `buf`. Every wave runs
+  // this (a window move needs all of them); the DMA waves issue the loads.
+  const bool dma = DW == kSWaves || wave >= kSWaves - DW;
+  const int dw = DW == kSWaves ? wave : wave - (kSWaves - DW);
+  const bool uniform_pages = (1 << shift) >= G::KPI;
+  int wbase = 0;  // window index held in win[0]
+  auto issue = [&](int g, int buf) {
+    const int s = seg_of(g);
+    const int lo = lane_val(sg.lo, s), last = lane_val(sg.hi, s) - 1;
+    const int woff = lane_val(sg.woff, s);
+    const int n0 = lo + (g - (lane_val(sg.incl, s) - lane_val(sg.nst, s))) * SK;
+    if (woff + (min(n0 + SK - 1, last) >> shift) - wbase >= kStreamPageWindow) {
+      // Long work item: move the window (drains the ring; once per window).
+      wait_vmcnt<0>();
+      __syncthreads();
+      wbase = woff + (min(n0, last) >> shift);
+      fill_window(win, a, w0, wbase, wcount);
+      __syncthreads();
+    }
+    if (dma)
+      issue_stage<KV, D, DW, SK>(a, win, wbase - woff, min(wcount - 1 - wbase, kStreamPageWindow - 1), h,
+                             n0, last, smem + buf * G::STAGE, dw, lane, uniform_pages);
+  };
+
+  // ---- start-up: NS - 1 stages (a short item repeats its last stage, so
+  // every DMA wave always issues the same number of loads here). The first
+  // segment's rows are older than every stage: waiting for all but the
+  // stages' loads leaves only the ring in flight.
   for (int g = 0; g < NS - 1; ++g) issue(min(g, nst_all - 1), g);
   if constexpr (DW == kSWaves) {
     wait_vmcnt<(NS - 1) * G::NPW>();
