@@ -1,4 +1,5 @@
-"""CPU oracle for verification attention over a paged KV cache.
+"""CPU oracle for verification attention over a paged KV cache and for the
+write of the drafts' keys and values into that cache.
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or links
 this package: only the tests, ``__graft_entry__.smoke()`` and the
@@ -9,7 +10,7 @@ seeded inputs drawn by ``workloads``.
 Every function here is pinned by CPU tests against facts that do not come
 from this code: worked tiny cases written as closed forms, library routines
 (``torch.nn.functional.scaled_dot_product_attention`` in float64,
-``torch.logsumexp``, torch's float8/bfloat16 casts) and the invariants the
+``torch.logsumexp``, torch's float8/bfloat16 casts and float32 division) and the invariants the
 pages state (chain mask = causal, paged = contiguous, GQA = expanded heads,
 single-query decode, split invariance, additive -inf/-5e4 masks).
 """
@@ -27,4 +28,12 @@ from .verify_attention import (  # noqa: F401
     verify_attention_partials,
     merge_partials,
     unpack_mask_block,
+)
+from .append_kv import (  # noqa: F401
+    append_kv,
+    quantise,
+    round_to_bf16,
+    round_to_e4m3fn_sat,
+    round_to_f32,
+    source_values,
 )

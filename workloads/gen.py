@@ -368,3 +368,45 @@ def kv_bytes(p: Problem) -> int:
         pages = int(p.kv_indptr[b + 1] - p.kv_indptr[b])
         kv_lens[b] = 0 if pages == 0 else (pages - 1) * p.page_size + int(p.last_page_len[b])
     return int(kv_lens.sum()) * p.num_kv_heads * p.head_dim * 2 * ELEM_BYTES[p.kv_dtype]
+
+
+# ---------------------------------------------------------------- new draft keys/values
+
+
+def make_append_inputs(p: Problem, src_dtype: str, seed: int, spread: float = 1.0,
+                       special: str = "none"):
+    """New keys and values ``[T, Hkv, D]`` for the drafts of ``p`` in ``src_dtype``.
+
+    ``spread`` scales N(0,1) draws (values beyond the cache's range exercise
+    saturation). ``special`` replaces the draws with bit patterns:
+    "all_bf16" cycles through all 65536 bfloat16 patterns (K takes the first
+    half of the cycle, V the second); "f32_bits" draws uniform random 32-bit
+    patterns (every class: NaN, infinities, subnormals, zeros).
+    """
+    g = torch.Generator().manual_seed(int(seed))
+    T = int(p.qo_indptr[-1])
+    shape = (T, p.num_kv_heads, p.head_dim)
+    n = T * p.num_kv_heads * p.head_dim
+    if special == "all_bf16":
+        if src_dtype != "bf16":
+            raise ValueError("all_bf16 needs a bf16 source")
+        pats = np.arange(2 * n, dtype=np.int64) % 65536
+        k = pats[:n].astype(np.uint16).reshape(shape)
+        v = pats[n:].astype(np.uint16).reshape(shape)
+        return k, v
+    if special == "f32_bits":
+        if src_dtype != "f32":
+            raise ValueError("f32_bits needs an f32 source")
+        bits = torch.randint(0, 1 << 32, (2, n), generator=g, dtype=torch.int64).numpy()
+        bits = bits.astype(np.uint32)
+        return bits[0].view(np.float32).reshape(shape), bits[1].view(np.float32).reshape(shape)
+    if special != "none":
+        raise ValueError(special)
+    k32 = torch.randn(shape, generator=g, dtype=torch.float32) * float(spread)
+    v32 = torch.randn(shape, generator=g, dtype=torch.float32) * float(spread)
+    if src_dtype == "f32":
+        return k32.numpy().copy(), v32.numpy().copy()
+    if src_dtype == "bf16":
+        return (k32.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy(),
+                v32.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy())
+    raise ValueError(src_dtype)
