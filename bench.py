@@ -19,6 +19,14 @@ from which the roofline fraction is computed with the algorithmic bytes
 
 Prints one JSON line. The oracle (single-threaded NumPy float64) is timed on
 the host on the same workload as the ``cpu_baseline`` leg.
+
+``--op append`` times the step before the path instead: ``vat_append_kv``
+writing the workload's draft keys and values (fresh seeded values, bf16, or
+fp32 for the fp32 workload) into its paged caches, rounded to the cache
+dtype. Copies of the sources and of the page table (a permutation of the
+pool per copy) rotate over the steps so successive steps write different
+pages. Every copy's result is checked bit for bit (copy 0 against the
+oracle, the others against copy 0 through their own page tables).
 """
 
 from __future__ import annotations
@@ -101,11 +109,191 @@ def timed_oracle(p, min_seconds: float, requests=None):
     return ref, (time.perf_counter() - t0), reps
 
 
+def append_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("device_common.h", "append_kernel.hip", "plan.h", "api.hip"):
+        with open(os.path.join(ROOT, "paged_kv_gqa_planner_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def hold_stream_timer(torch, K, launches, host_per_launch):
+    """Average GPU ms per launch of K back-to-back launches (``launches(i)``
+    enqueues launch i); the stream is held by a GPU sleep while the host
+    queues them, so the events time GPU work only."""
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    torch.cuda._sleep(1_000_000)
+    c1.record()
+    torch.cuda.synchronize()
+    cycles_per_ms = 1_000_000 / max(c0.elapsed_time(c1), 1e-3)
+    hold_ms = 20.0 + 2.0 * K * host_per_launch * 1e3
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(hold_ms * cycles_per_ms))
+    start.record()
+    t_enq = time.perf_counter()
+    for i in range(K):
+        launches(i)
+    end.record()
+    enqueue_ms = (time.perf_counter() - t_enq) * 1e3
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / K, enqueue_ms < hold_ms
+
+
+def bench_append(args, p, dev):
+    """--op append: the draft key/value write into the paged cache."""
+    import torch
+
+    from oracle import append_kv as oracle_append
+    from paged_kv_gqa_planner_amd import binding
+    from tests.gpu_helpers import to_device
+    from workloads import make_append_inputs
+
+    src = "f32" if p.kv_dtype == "f32" else "bf16"
+    spread = 2.0 if p.kv_dtype == "e4m3" else 1.0
+    ks, vs = p.k_scale, p.v_scale
+    T = p.num_tokens
+    k_new, v_new = make_append_inputs(p, src, seed=1000 + args.config, spread=spread)
+    base = to_device(p, dev)
+    se = 4 if src == "f32" else 2
+    ce = {"f32": 4, "bf16": 2, "e4m3": 1}[p.kv_dtype]
+    elems = 2 * T * p.num_kv_heads * p.head_dim
+    alg_bytes = elems * (se + ce) + 4 * T  # sources read, cache rows written, page ids
+    touched = elems * (se + ce)
+    copies = args.copies or max(2, math.ceil((1 << 30) / max(touched, 1)))
+    copies = min(copies, 64)
+
+    def dev_src(a):
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16 if src == "bf16" else np.float32))
+        return (t.view(torch.bfloat16) if src == "bf16" else t).to(dev)
+
+    gen = torch.Generator(device="cpu").manual_seed(4321)
+    used = int(p.kv_indptr[-1])
+    calls, tables = [], []
+    for i in range(copies):
+        if i == 0:
+            idx = base["kv_indices"]
+        else:
+            perm = torch.randperm(p.num_pages, generator=gen).to(dev)
+            idx = base["kv_indices"].clone()
+            idx[:used] = perm[base["kv_indices"][:used].long()].to(torch.int32)
+        kn, vn = dev_src(k_new), dev_src(v_new)
+        tables.append(idx)
+        calls.append(binding.PreparedAppend(kn, vn, base["k_cache"], base["v_cache"],
+                                            base["kv_indptr"], idx, base["last_page_len"],
+                                            base["qo_indptr"], k_scale=ks, v_scale=vs,
+                                            max_qo_len=p.max_qo_len))
+    torch.cuda.synchronize()
+
+    def raw(t):
+        return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else (
+            t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32))
+
+    # ---- verification. Copy 0 on a fresh cache against the oracle (every
+    # byte); each other copy's written rows, read back through its own page
+    # table, against copy 0's.
+    calls[0]()
+    torch.cuda.synchronize()
+    got_k = raw(base["k_cache"]).cpu().numpy()
+    got_v = raw(base["v_cache"]).cpu().numpy()
+    t_cpu = time.perf_counter()
+    reps = 0
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(1):
+        while True:
+            want_k, want_v = oracle_append(k_new, v_new, src, p.k_cache, p.v_cache, p.kv_dtype,
+                                           p.kv_indptr, p.kv_indices, p.last_page_len,
+                                           p.qo_indptr, p.page_size, k_scale=ks, v_scale=vs)
+            reps += 1
+            if args.no_cpu_baseline or time.perf_counter() - t_cpu >= args.cpu_seconds:
+                break
+    cpu_s = time.perf_counter() - t_cpu
+
+    def words(a):
+        return a.view(np.uint8) if a.dtype == np.uint8 else (
+            a.view(np.int16) if a.dtype == np.uint16 else a.view(np.int32))
+
+    verified = bool(np.array_equal(got_k, words(want_k)) and np.array_equal(got_v, words(want_v)))
+    rows_page, rows_slot = [], []
+    for b in range(p.batch):
+        L = int(p.qo_indptr[b + 1] - p.qo_indptr[b])
+        pages = int(p.kv_indptr[b + 1] - p.kv_indptr[b])
+        kv_len = 0 if pages == 0 else (pages - 1) * p.page_size + int(p.last_page_len[b])
+        for t in range(L):
+            n = kv_len - L + t
+            rows_page.append(int(p.kv_indptr[b]) + n // p.page_size)
+            rows_slot.append(n % p.page_size)
+    rp = torch.tensor(rows_page, dtype=torch.long, device=dev)
+    rs = torch.tensor(rows_slot, dtype=torch.long, device=dev)
+
+    def written(idx):
+        pg = idx[rp].long()
+        return raw(base["k_cache"])[pg, rs].clone(), raw(base["v_cache"])[pg, rs].clone()
+
+    ref_rows = written(tables[0])
+    for i in range(1, copies):
+        calls[i]()
+        torch.cuda.synchronize()
+        k_rows, v_rows = written(tables[i])
+        verified = verified and torch.equal(k_rows, ref_rows[0]) and torch.equal(v_rows, ref_rows[1])
+
+    # ---- warmup and timed region (K launches back to back)
+    for i in range(args.warmup):
+        calls[i % copies]()
+    torch.cuda.synchronize()
+    t_host = time.perf_counter()
+    for i in range(3):
+        calls[i % copies]()
+    host_per = (time.perf_counter() - t_host) / 3
+    torch.cuda.synchronize()
+    K = args.steps
+    ms, ahead = hold_stream_timer(torch, K, lambda i: calls[i % copies](), host_per)
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "appended draft tokens/s (K and V rounded into the paged cache), 1 MI355X",
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"{src}->{p.kv_dtype}",
+        "data": "synthetic",
+        "config": {"workload": "draft K/V write of: " +
+                   WORKLOAD_NAMES[args.config].format(p=args.prefix),
+                   "tokens": T, "kv_heads": p.num_kv_heads, "head_dim": p.head_dim,
+                   "source_copies": copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "kernel": "vat_append",
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "verified": verified,
+        "gpu_ran_ahead_of_host": bool(ahead),
+        "kernel_source": append_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = {
+            "value": round(T * reps / cpu_s, 1), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"whole workload, repeated {reps}x, {cpu_s:.1f} s, NumPy, one thread"}
+    print(json.dumps(line), flush=True)
+    if not verified:
+        sys.exit(3)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--op", default="verify", choices=["verify", "append"],
+                    help="verify: the attention path; append: the draft K/V cache write")
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--prefix", type=int, default=4096, help="prefix length for config 3")
     ap.add_argument("--copies", type=int, default=0,
@@ -149,6 +337,9 @@ def main():
         return
 
     p = make_config(args.config, prefix=args.prefix)
+    if args.op == "append":
+        bench_append(args, p, dev)
+        return
     kvb, flops = algorithmic_work(p)
     tokens = p.num_tokens
     base = to_device(p, dev)

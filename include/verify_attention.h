@@ -181,6 +181,38 @@ vat_status_t vat_launch_merge(const vat_problem_t* problem, const int32_t* kv_in
                               float v_scale, void* out, float* lse, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* Write the drafts' keys and values into the paged caches, rounded to the
+ * cache dtype: the step before verification attention, which expects every
+ * draft's key and value to be cached already (vLLM page "[WIP] Support for
+ * cached multi-query attention towards speculative decoding").
+ *
+ * Row qo_indptr[b] + t of k_new / v_new ([T, Hkv, D], dense, in src_dtype:
+ * VAT_F32 or VAT_BF16) is written to key position n = kv_len_b - L_b + t of
+ * request b: slot n % page_size of page kv_indices[kv_indptr[b] + n /
+ * page_size] (the paged format documented above), for t = 0 .. L_b - 1. The
+ * stored element is x / scale (k_scale for keys, v_scale for values), the
+ * inverse of the attention's read of scale * stored (flashmap page
+ * "sglang/verify_attention.py", k_scale / v_scale folding): one IEEE binary32
+ * division, then round-to-nearest-even into problem->kv_dtype -- fp32 as is,
+ * bf16 (overflow to infinity as IEEE), e4m3fn after clamping to [-448, 448]
+ * (saturating: the format has no infinity). A NaN input stores the canonical
+ * quiet NaN of the cache dtype (0x7FC00000, 0x7FC0, 0x7F) with the input's
+ * sign. Nothing else in the caches changes.
+ *
+ * Reads batch, num_kv_heads, head_dim (64 or 128), page_size, num_pages,
+ * num_kv_indices, num_qo_tokens, max_qo_len (sizes the launch; rows beyond
+ * it are still written) and kv_dtype of *problem; the other fields are
+ * ignored. k_scale and v_scale must be finite and > 0. k_new, v_new and the
+ * caches must be 16-byte aligned. The same device-content contract as
+ * verify_attention holds; index violations give unspecified cache contents
+ * inside the caches, never an access outside them. Enqueues one kernel on
+ * `stream`; allocates nothing; capturable. */
+vat_status_t vat_append_kv(const vat_problem_t* problem, int32_t src_dtype, const void* k_new,
+                           const void* v_new, void* k_cache, void* v_cache,
+                           const int32_t* kv_indptr, const int32_t* kv_indices,
+                           const int32_t* last_page_len, const int32_t* qo_indptr, float k_scale,
+                           float v_scale, void* stream);
+
 /* Static description of a status code. */
 const char* vat_status_string(vat_status_t status);
 

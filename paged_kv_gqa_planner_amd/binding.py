@@ -78,6 +78,9 @@ def load(path: Optional[str] = None):
     lib.vat_launch_partial.restype = ctypes.c_int
     lib.vat_launch_merge.argtypes = [P(VatProblem), vp, vp, vp, f, vp, vp, vp, ctypes.c_size_t, vp]
     lib.vat_launch_merge.restype = ctypes.c_int
+    lib.vat_append_kv.argtypes = [P(VatProblem), ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  f, f, vp]
+    lib.vat_append_kv.restype = ctypes.c_int
     lib.vat_status_string.argtypes = [ctypes.c_int]
     lib.vat_status_string.restype = ctypes.c_char_p
     lib.vat_abi_version.argtypes = []
@@ -230,6 +233,72 @@ def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, 
                               _stream_handle(stream))
     _check(st, "verify_attention")
     return out, lse
+
+
+def append_problem(k_new, k_cache, kv_indptr, kv_indices, max_qo_len=None) -> VatProblem:
+    """Problem record for vat_append_kv from the tensors' shapes."""
+    if k_new.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("k_new must be [T, Hkv, D] and caches [pages, page_size, Hkv, D]")
+    batch = kv_indptr.numel() - 1
+    T = k_new.shape[0]
+    if max_qo_len is None:
+        max_qo_len = T - (batch - 1) if batch > 0 else 0
+    hkv, d = k_cache.shape[2], k_cache.shape[3]
+    return make_problem(batch=batch, num_qo_heads=hkv, num_kv_heads=hkv, head_dim=d,
+                        page_size=k_cache.shape[1], num_pages=k_cache.shape[0],
+                        num_kv_indices=kv_indices.numel(), num_qo_tokens=T,
+                        max_qo_len=max(int(max_qo_len), 0), q_dtype=_dtype_code(k_new),
+                        kv_dtype=_dtype_code(k_cache), has_mask=0)
+
+
+def _append_args(k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
+                 qo_indptr, k_scale, v_scale, max_qo_len, stream):
+    import torch
+
+    idx = [("kv_indptr", kv_indptr), ("kv_indices", kv_indices),
+           ("last_page_len", last_page_len), ("qo_indptr", qo_indptr)]
+    _check_tensors(k_new, k_cache, v_cache, idx + [("v_new", v_new)])
+    for name, t in idx:
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be torch.int32")
+    if v_new.shape != k_new.shape or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new and v_new must have one shape and dtype")
+    if k_new.shape[1:] != k_cache.shape[2:]:
+        raise ValueError("k_new rows must be [Hkv, D] of the cache")
+    problem = append_problem(k_new, k_cache, kv_indptr, kv_indices, max_qo_len)
+    return problem, (ctypes.byref(problem), _dtype_code(k_new), _ptr(k_new), _ptr(v_new),
+                     _ptr(k_cache), _ptr(v_cache), _ptr(kv_indptr), _ptr(kv_indices),
+                     _ptr(last_page_len), _ptr(qo_indptr), float(k_scale), float(v_scale),
+                     _stream_handle(stream))
+
+
+def append_kv(k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr,
+              k_scale: float = 1.0, v_scale: float = 1.0, max_qo_len: Optional[int] = None,
+              stream=None):
+    """Write the drafts' keys/values ``[T, Hkv, D]`` (fp32 or bf16) into the
+    paged caches in place, stored as ``x / scale`` rounded to the cache dtype.
+    ``max_qo_len`` defaults to the shape-only bound ``T - (B - 1)``."""
+    lib = load()
+    problem, args = _append_args(k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices,
+                                 last_page_len, qo_indptr, k_scale, v_scale, max_qo_len, stream)
+    _check(lib.vat_append_kv(*args), "vat_append_kv")
+    return k_cache, v_cache
+
+
+class PreparedAppend:
+    """vat_append_kv with every argument fixed (checked once), for timing."""
+
+    def __init__(self, k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
+                 qo_indptr, k_scale=1.0, v_scale=1.0, max_qo_len=None, stream=None):
+        self.lib = load()
+        self.keep = (k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
+                     qo_indptr)
+        self.problem, self.args = _append_args(k_new, v_new, k_cache, v_cache, kv_indptr,
+                                               kv_indices, last_page_len, qo_indptr, k_scale,
+                                               v_scale, max_qo_len, stream)
+
+    def __call__(self):
+        _check(self.lib.vat_append_kv(*self.args), "vat_append_kv")
 
 
 class PreparedCall:

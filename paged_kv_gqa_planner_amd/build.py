@@ -22,7 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvat.so")
 ARCH = "gfx950"
 
-SOURCES = ["plan.cpp", "tile_kernel.hip", "stream_kernel.hip", "merge_kernel.hip", "api.hip"]
+SOURCES = ["plan.cpp", "tile_kernel.hip", "stream_kernel.hip", "merge_kernel.hip", "append_kernel.hip",
+           "api.hip"]
 
 
 def hipcc() -> str:

@@ -12,6 +12,7 @@ namespace vat {
 const void* tile_kernel(int kv_dtype, int head_dim, int rt);
 const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int pair);
 const void* merge_kernel(int q_is_f32, int head_dim);
+const void* append_kernel(int src_dtype, int cache_dtype);
 }  // namespace vat
 
 namespace {
@@ -246,6 +247,52 @@ vat_status_t verify_attention(const vat_problem_t* problem, const void* q, const
   if (st != VAT_OK) return st;
   return launch_merge(problem, plan, kv_indptr, last_page_len, qo_indptr, v_scale, out, lse,
                       workspace, (hipStream_t)stream);
+}
+
+vat_status_t vat_append_kv(const vat_problem_t* problem, int32_t src_dtype, const void* k_new,
+                           const void* v_new, void* k_cache, void* v_cache,
+                           const int32_t* kv_indptr, const int32_t* kv_indices,
+                           const int32_t* last_page_len, const int32_t* qo_indptr, float k_scale,
+                           float v_scale, void* stream) {
+  vat_status_t st = vat::validate_append(problem, src_dtype);
+  if (st != VAT_OK) return st;
+  if (!(k_scale > 0.f) || !isfinite(k_scale) || !(v_scale > 0.f) || !isfinite(v_scale))
+    return VAT_ERR_SHAPE;
+  const vat_problem_t& p = *problem;
+  if (p.batch == 0 || p.num_qo_tokens == 0 || p.max_qo_len == 0) return VAT_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !kv_indptr || !kv_indices || !last_page_len ||
+      !qo_indptr)
+    return VAT_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(kv_indptr, 4) || !aligned(kv_indices, 4) ||
+      !aligned(last_page_len, 4) || !aligned(qo_indptr, 4))
+    return VAT_ERR_ALIGN;
+  vat::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.last_page_len = last_page_len;
+  a.qo_indptr = qo_indptr;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.batch = p.batch;
+  a.row_units = p.num_kv_heads * p.head_dim / 8;
+  a.page_shift = page_shift(p.page_size);
+  a.num_pages = p.num_pages;
+  a.num_kv_indices = p.num_kv_indices;
+  a.tokens = p.num_qo_tokens;
+  // Grid y covers max_qo_len tokens of K and V per request; the kernel loops
+  // over any remainder, so the bound only sizes the launch.
+  const int64_t units = 2 * int64_t(p.max_qo_len) * a.row_units;
+  const int64_t gy = (units + vat::kAppendThreads - 1) / vat::kAppendThreads;
+  const void* fn = vat::append_kernel(src_dtype, p.kv_dtype);
+  void* args[] = {&a};
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.batch, (unsigned)(gy < 65535 ? gy : 65535), 1),
+                                 dim3(vat::kAppendThreads, 1, 1), args, 0, (hipStream_t)stream);
+  return e == hipSuccess ? VAT_OK : VAT_ERR_HIP;
 }
 
 const char* vat_status_string(vat_status_t status) {

@@ -45,6 +45,24 @@ vat_status_t validate_problem(const vat_problem_t* p) {
   return VAT_OK;
 }
 
+vat_status_t validate_append(const vat_problem_t* p, int32_t src_dtype) {
+  if (!p) return VAT_ERR_NULL;
+  if (p->batch < 0 || p->num_kv_heads < 1 || p->num_pages < 0 || p->num_kv_indices < 0 ||
+      p->num_qo_tokens < 0 || p->max_qo_len < 0)
+    return VAT_ERR_SHAPE;
+  if (p->head_dim != 64 && p->head_dim != 128) return VAT_ERR_UNSUPPORTED;
+  if (!is_pow2(p->page_size) || p->page_size > 256) return VAT_ERR_UNSUPPORTED;
+  if (src_dtype != VAT_F32 && src_dtype != VAT_BF16) return VAT_ERR_UNSUPPORTED;
+  if (p->kv_dtype != VAT_F32 && p->kv_dtype != VAT_BF16 && p->kv_dtype != VAT_FP8_E4M3FN)
+    return VAT_ERR_UNSUPPORTED;
+  if (p->batch > 0 && p->num_qo_tokens > 0 && p->num_pages < 1) return VAT_ERR_SHAPE;
+  if (int64_t(p->num_kv_indices) * p->page_size > int64_t(INT32_MAX) / 2) return VAT_ERR_SHAPE;
+  // Key positions and token rows are int32 inside the kernel.
+  if (int64_t(p->max_qo_len) * p->num_kv_heads * p->head_dim > int64_t(INT32_MAX))
+    return VAT_ERR_SHAPE;
+  return VAT_OK;
+}
+
 vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan) {
   if (!plan) return VAT_ERR_NULL;
   vat_status_t st = validate_problem(p);

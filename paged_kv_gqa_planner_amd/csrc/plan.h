@@ -82,8 +82,34 @@ struct MergeArgs {
   int32_t slices;  // > 0: partials come from balanced page slices, slot = slice + request
 };
 
+// Arguments of the draft key/value write (cache append) kernel.
+struct AppendArgs {
+  const void* k_new;  // [T, Hkv, D] in the source dtype
+  const void* v_new;
+  void* k_cache;      // [num_pages, page_size, Hkv, D] in the cache dtype
+  void* v_cache;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* last_page_len;
+  const int32_t* qo_indptr;
+  float k_scale, v_scale;
+  int32_t batch;
+  int32_t row_units;  // Hkv * D / 8: 8-element units in one token row
+  int32_t page_shift;
+  int32_t num_pages;
+  int32_t num_kv_indices;
+  int32_t tokens;
+};
+
+constexpr int kAppendThreads = 256;
+
 // Shape validation (host-detectable errors only).
 vat_status_t validate_problem(const vat_problem_t* p);
+
+// Validation of the fields the cache append reads (batch, num_kv_heads,
+// head_dim, page_size, num_pages, num_kv_indices, num_qo_tokens, max_qo_len,
+// kv_dtype) and of the source dtype.
+vat_status_t validate_append(const vat_problem_t* p, int32_t src_dtype);
 
 // Shape-only plan for `num_cus` compute units. Calls validate_problem.
 vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan);

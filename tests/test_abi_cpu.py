@@ -39,7 +39,8 @@ def header_functions():
 def test_library_exports_every_header_function(lib):
     names = header_functions()
     assert {"verify_attention", "vat_plan", "vat_workspace_size", "vat_launch_partial",
-            "vat_launch_merge", "vat_status_string", "vat_abi_version"} <= set(names)
+            "vat_launch_merge", "vat_append_kv", "vat_status_string",
+            "vat_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert lib.vat_abi_version() == 1
@@ -248,6 +249,52 @@ def test_empty_work_returns_ok_without_a_gpu(lib):
     assert _call(lib, base_problem(num_qo_tokens=0), ptrs=dict(q=0, out=0, lse=0)) == 0
     assert _call(lib, base_problem(batch=0, num_qo_tokens=0)) == 0
     assert _call(lib, base_problem(max_qo_len=0)) == 0
+
+
+def _append(lib, prob, src=1, ptrs=None, scales=(1.0, 1.0)):
+    fake = 0x10000
+    p = dict(kn=fake, vn=fake, kc=fake, vc=fake, indptr=fake, indices=fake, lpl=fake, qo=fake)
+    if ptrs:
+        p.update(ptrs)
+    return lib.vat_append_kv(ctypes.byref(prob), src, p["kn"], p["vn"], p["kc"], p["vc"],
+                             p["indptr"], p["indices"], p["lpl"], p["qo"], scales[0], scales[1],
+                             None)
+
+
+@pytest.mark.parametrize("kw,src,code", [
+    (dict(head_dim=96), 1, 3),
+    (dict(page_size=12), 1, 3),
+    (dict(kv_dtype=3), 1, 3),
+    ({}, 2, 3),            # an e4m3 source is not accepted
+    ({}, 7, 3),
+    (dict(batch=-1), 1, 2),
+    (dict(num_pages=0), 1, 2),
+    (dict(num_kv_heads=0), 1, 2),
+    (dict(max_qo_len=-1), 1, 2),
+])
+def test_append_rejects_invalid_problems(lib, kw, src, code):
+    assert _append(lib, base_problem(**kw), src=src) == code
+
+
+def test_append_host_checks_before_any_launch(lib):
+    prob = base_problem(kv_dtype=2)
+    assert _append(lib, prob, ptrs=dict(kn=0)) == 1
+    assert _append(lib, prob, ptrs=dict(vc=0)) == 1
+    assert _append(lib, prob, ptrs=dict(qo=0)) == 1
+    assert _append(lib, prob, ptrs=dict(kn=0x10008)) == 4
+    assert _append(lib, prob, ptrs=dict(kc=0x10001)) == 4
+    assert _append(lib, prob, ptrs=dict(indices=0x10002)) == 4
+    for sc in [(0.0, 1.0), (-1.0, 1.0), (1.0, float("inf")), (float("nan"), 1.0)]:
+        assert _append(lib, prob, scales=sc) == 2
+    # The fields the append does not read are not checked.
+    assert _append(lib, base_problem(num_qo_heads=3, num_kv_heads=2, q_dtype=0, kv_dtype=2,
+                                     chunk_keys=-7), ptrs=dict(kn=0)) == 1
+
+
+def test_append_of_nothing_returns_ok_without_a_gpu(lib):
+    assert _append(lib, base_problem(num_qo_tokens=0), ptrs=dict(kn=0, vn=0)) == 0
+    assert _append(lib, base_problem(batch=0, num_qo_tokens=0)) == 0
+    assert _append(lib, base_problem(max_qo_len=0)) == 0
 
 
 def test_planner_under_address_and_ub_sanitizers(tmp_path):
