@@ -201,8 +201,8 @@ vat_status_t vat_launch_merge(const vat_problem_t* problem, const int32_t* kv_in
  *
  * Reads batch, num_kv_heads, head_dim (64 or 128), page_size, num_pages,
  * num_kv_indices, num_qo_tokens, max_qo_len (sizes the launch; rows beyond
- * it are still written) and kv_dtype of *problem; the other fields are
- * ignored. k_scale and v_scale must be finite and > 0. k_new, v_new and the
+ * it are still written), kv_dtype and num_cus (0 = query the current device)
+ * of *problem; the other fields are ignored. k_scale and v_scale must be finite and > 0. k_new, v_new and the
  * caches must be 16-byte aligned. The same device-content contract as
  * verify_attention holds; index violations give unspecified cache contents
  * inside the caches, never an access outside them. Enqueues one kernel on

@@ -235,7 +235,8 @@ def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, 
     return out, lse
 
 
-def append_problem(k_new, k_cache, kv_indptr, kv_indices, max_qo_len=None) -> VatProblem:
+def append_problem(k_new, k_cache, kv_indptr, kv_indices, max_qo_len=None,
+                   num_cus=0) -> VatProblem:
     """Problem record for vat_append_kv from the tensors' shapes."""
     if k_new.dim() != 3 or k_cache.dim() != 4:
         raise ValueError("k_new must be [T, Hkv, D] and caches [pages, page_size, Hkv, D]")
@@ -248,11 +249,11 @@ def append_problem(k_new, k_cache, kv_indptr, kv_indices, max_qo_len=None) -> Va
                         page_size=k_cache.shape[1], num_pages=k_cache.shape[0],
                         num_kv_indices=kv_indices.numel(), num_qo_tokens=T,
                         max_qo_len=max(int(max_qo_len), 0), q_dtype=_dtype_code(k_new),
-                        kv_dtype=_dtype_code(k_cache), has_mask=0)
+                        kv_dtype=_dtype_code(k_cache), has_mask=0, num_cus=num_cus)
 
 
 def _append_args(k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
-                 qo_indptr, k_scale, v_scale, max_qo_len, stream):
+                 qo_indptr, k_scale, v_scale, max_qo_len, stream, num_cus=0):
     import torch
 
     idx = [("kv_indptr", kv_indptr), ("kv_indices", kv_indices),
@@ -265,7 +266,7 @@ def _append_args(k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices, last_pag
         raise ValueError("k_new and v_new must have one shape and dtype")
     if k_new.shape[1:] != k_cache.shape[2:]:
         raise ValueError("k_new rows must be [Hkv, D] of the cache")
-    problem = append_problem(k_new, k_cache, kv_indptr, kv_indices, max_qo_len)
+    problem = append_problem(k_new, k_cache, kv_indptr, kv_indices, max_qo_len, num_cus)
     return problem, (ctypes.byref(problem), _dtype_code(k_new), _ptr(k_new), _ptr(v_new),
                      _ptr(k_cache), _ptr(v_cache), _ptr(kv_indptr), _ptr(kv_indices),
                      _ptr(last_page_len), _ptr(qo_indptr), float(k_scale), float(v_scale),
@@ -274,13 +275,15 @@ def _append_args(k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices, last_pag
 
 def append_kv(k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr,
               k_scale: float = 1.0, v_scale: float = 1.0, max_qo_len: Optional[int] = None,
-              stream=None):
+              stream=None, num_cus: int = 0):
     """Write the drafts' keys/values ``[T, Hkv, D]`` (fp32 or bf16) into the
     paged caches in place, stored as ``x / scale`` rounded to the cache dtype.
-    ``max_qo_len`` defaults to the shape-only bound ``T - (B - 1)``."""
+    ``max_qo_len`` defaults to the shape-only bound ``T - (B - 1)``;
+    ``num_cus`` 0 sizes the launch for the current device."""
     lib = load()
     problem, args = _append_args(k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices,
-                                 last_page_len, qo_indptr, k_scale, v_scale, max_qo_len, stream)
+                                 last_page_len, qo_indptr, k_scale, v_scale, max_qo_len, stream,
+                                 num_cus)
     _check(lib.vat_append_kv(*args), "vat_append_kv")
     return k_cache, v_cache
 
@@ -289,13 +292,13 @@ class PreparedAppend:
     """vat_append_kv with every argument fixed (checked once), for timing."""
 
     def __init__(self, k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
-                 qo_indptr, k_scale=1.0, v_scale=1.0, max_qo_len=None, stream=None):
+                 qo_indptr, k_scale=1.0, v_scale=1.0, max_qo_len=None, stream=None, num_cus=0):
         self.lib = load()
         self.keep = (k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
                      qo_indptr)
         self.problem, self.args = _append_args(k_new, v_new, k_cache, v_cache, kv_indptr,
                                                kv_indices, last_page_len, qo_indptr, k_scale,
-                                               v_scale, max_qo_len, stream)
+                                               v_scale, max_qo_len, stream, num_cus)
 
     def __call__(self):
         _check(self.lib.vat_append_kv(*self.args), "vat_append_kv")

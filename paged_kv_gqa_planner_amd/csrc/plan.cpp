@@ -48,7 +48,7 @@ vat_status_t validate_problem(const vat_problem_t* p) {
 vat_status_t validate_append(const vat_problem_t* p, int32_t src_dtype) {
   if (!p) return VAT_ERR_NULL;
   if (p->batch < 0 || p->num_kv_heads < 1 || p->num_pages < 0 || p->num_kv_indices < 0 ||
-      p->num_qo_tokens < 0 || p->max_qo_len < 0)
+      p->num_qo_tokens < 0 || p->max_qo_len < 0 || p->num_cus < 0)
     return VAT_ERR_SHAPE;
   if (p->head_dim != 64 && p->head_dim != 128) return VAT_ERR_UNSUPPORTED;
   if (!is_pow2(p->page_size) || p->page_size > 256) return VAT_ERR_UNSUPPORTED;

@@ -93,6 +93,7 @@ struct AppendArgs {
   const int32_t* last_page_len;
   const int32_t* qo_indptr;
   float k_scale, v_scale;
+  float k_inv, v_inv;  // exact 1 / scale when both scales are powers of two
   int32_t batch;
   int32_t row_units;  // Hkv * D / 8: 8-element units in one token row
   int32_t page_shift;
@@ -108,7 +109,7 @@ vat_status_t validate_problem(const vat_problem_t* p);
 
 // Validation of the fields the cache append reads (batch, num_kv_heads,
 // head_dim, page_size, num_pages, num_kv_indices, num_qo_tokens, max_qo_len,
-// kv_dtype) and of the source dtype.
+// kv_dtype, num_cus) and of the source dtype.
 vat_status_t validate_append(const vat_problem_t* p, int32_t src_dtype);
 
 // Shape-only plan for `num_cus` compute units. Calls validate_problem.

@@ -271,6 +271,7 @@ def _append(lib, prob, src=1, ptrs=None, scales=(1.0, 1.0)):
     (dict(num_pages=0), 1, 2),
     (dict(num_kv_heads=0), 1, 2),
     (dict(max_qo_len=-1), 1, 2),
+    (dict(num_cus=-1), 1, 2),
 ])
 def test_append_rejects_invalid_problems(lib, kw, src, code):
     assert _append(lib, base_problem(**kw), src=src) == code

@@ -42,19 +42,20 @@ def _words(a: np.ndarray) -> np.ndarray:
     return a.view(np.uint32) if a.dtype == np.float32 else a
 
 
-def _run(lib, p, k_new, v_new, src, ks, vs, max_qo_len=None, tensors=None):
+def _run(lib, p, k_new, v_new, src, ks, vs, max_qo_len=None, tensors=None, num_cus=0):
     t = tensors if tensors is not None else to_device(p)
     lib.append_kv(_src_tensor(k_new, src), _src_tensor(v_new, src), t["k_cache"], t["v_cache"],
                   t["kv_indptr"], t["kv_indices"], t["last_page_len"], t["qo_indptr"],
-                  k_scale=ks, v_scale=vs, max_qo_len=max_qo_len)
+                  k_scale=ks, v_scale=vs, max_qo_len=max_qo_len, num_cus=num_cus)
     torch.cuda.synchronize()
     return t
 
 
-def _check(lib, p, k_new, v_new, src, ks, vs, what, max_qo_len=None):
+def _check(lib, p, k_new, v_new, src, ks, vs, what, max_qo_len=None, num_cus=0):
     say(f"[append {what}] {p.name or 'case'} src={src} cache={p.kv_dtype} "
-        f"T={int(p.qo_indptr[-1])} scales=({ks:.6g}, {vs:.6g}) max_qo_len={max_qo_len}")
-    t = _run(lib, p, k_new, v_new, src, ks, vs, max_qo_len=max_qo_len)
+        f"T={int(p.qo_indptr[-1])} scales=({ks:.6g}, {vs:.6g}) max_qo_len={max_qo_len} "
+        f"num_cus={num_cus}")
+    t = _run(lib, p, k_new, v_new, src, ks, vs, max_qo_len=max_qo_len, num_cus=num_cus)
     got_k, got_v = _raw(t["k_cache"]), _raw(t["v_cache"])
     want_k, want_v = oracle_append(k_new, v_new, src, p.k_cache, p.v_cache, p.kv_dtype,
                                    p.kv_indptr, p.kv_indices, p.last_page_len, p.qo_indptr,
@@ -112,25 +113,47 @@ def _pattern_case(cache_dtype, page_size=16, head_dim=128):
                      name=f"patterns-{cache_dtype}-ps{page_size}-d{head_dim}")
 
 
+# The write takes two units per thread when it covers every CU several times
+# over; planning for one CU makes these small cases take that variant too.
+NUM_CUS = [0, 1]
+
+
+@pytest.mark.parametrize("num_cus", NUM_CUS)
 @pytest.mark.parametrize("cache_dtype", ["bf16", "e4m3", "f32"])
 @pytest.mark.parametrize("scale", [1.0, 0.0123, 3.75])
-def test_every_bf16_pattern(gpu_lib, cache_dtype, scale):
+def test_every_bf16_pattern(gpu_lib, cache_dtype, scale, num_cus):
     """All 65536 bfloat16 inputs (NaNs, infinities, subnormals, both zeros)
-    divided by the scale and stored."""
+    divided by the scale and stored (scale 1 takes the exact-reciprocal
+    path: both scales are powers of two)."""
     p = _pattern_case(cache_dtype)
     k_new, v_new = make_append_inputs(p, "bf16", seed=0, special="all_bf16")
     _check(gpu_lib, p, k_new, v_new, "bf16", scale, float(np.float32(scale * 0.5)),
-           f"all bf16 patterns scale {scale}")
+           f"all bf16 patterns scale {scale}", num_cus=num_cus)
 
 
+@pytest.mark.parametrize("num_cus", NUM_CUS)
 @pytest.mark.parametrize("cache_dtype", ["bf16", "e4m3", "f32"])
-@pytest.mark.parametrize("seed,scale", [(1, 1.0), (2, 3.75), (3, 1e-3), (4, 2.0 ** -20)])
-def test_random_f32_bit_patterns(gpu_lib, cache_dtype, seed, scale):
+@pytest.mark.parametrize("seed,scale", [(1, 1.0), (2, 3.75), (3, 1e-3), (4, 2.0 ** -20),
+                                        (5, 2.0 ** 100)])
+def test_random_f32_bit_patterns(gpu_lib, cache_dtype, seed, scale, num_cus):
     """Uniformly random 32-bit inputs: every class of binary32 value, and
-    quotients that underflow to subnormals (checks the division keeps them)."""
+    quotients that underflow to subnormals or overflow (checks both the
+    division and the exact-reciprocal multiply keep IEEE results)."""
     p = _pattern_case(cache_dtype)
     k_new, v_new = make_append_inputs(p, "f32", seed=seed, special="f32_bits")
-    _check(gpu_lib, p, k_new, v_new, "f32", scale, scale, f"random f32 bits seed {seed}")
+    _check(gpu_lib, p, k_new, v_new, "f32", scale, scale, f"random f32 bits seed {seed}",
+           num_cus=num_cus)
+
+
+@pytest.mark.parametrize("scales", [(1.0, 0.75), (0.0123, 0.5), (2.0 ** -126, 2.0 ** 126),
+                                    (2.0 ** 127, 1.0), (2.0 ** -130, 1.0)])
+def test_mixed_and_extreme_scales(gpu_lib, scales):
+    """Only both scales being normal powers of two with normal reciprocals
+    takes the multiply; the extreme ones (2^127, a subnormal 2^-130) divide."""
+    p = _pattern_case("e4m3")
+    k_new, v_new = make_append_inputs(p, "f32", seed=6, special="f32_bits")
+    ks, vs = (float(np.float32(x)) for x in scales)
+    _check(gpu_lib, p, k_new, v_new, "f32", ks, vs, f"scales {scales}")
 
 
 # ---------------------------------------------------------------- layout edges
@@ -158,6 +181,7 @@ def test_long_requests_use_many_workgroups(gpu_lib):
                   name="long-drafts")
     k_new, v_new = make_append_inputs(p, "bf16", seed=9, spread=1.5)
     _check(gpu_lib, p, k_new, v_new, "bf16", 0.0123, 0.0071, "long requests")
+    _check(gpu_lib, p, k_new, v_new, "bf16", 0.0123, 0.0071, "long requests, 1 CU", num_cus=1)
 
 
 def test_no_drafts_changes_nothing(gpu_lib):
