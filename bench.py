@@ -102,7 +102,7 @@ def timed_oracle(p, min_seconds: float, requests=None):
             ref = oracle_va(p.q, p.k_cache, p.v_cache, p.kv_indptr, p.kv_indices, p.last_page_len,
                             p.qo_indptr, p.mask, p.mask_indptr, sm_scale=p.sm_scale,
                             k_scale=p.k_scale, v_scale=p.v_scale, q_dtype=p.q_dtype,
-                            kv_dtype=p.kv_dtype, requests=requests)
+                            kv_dtype=p.kv_dtype, requests=requests, mask_layout=p.mask_layout)
             reps += 1
             if time.perf_counter() - t0 >= min_seconds:
                 break

@@ -28,6 +28,8 @@ from .verify_attention import (  # noqa: F401
     verify_attention_partials,
     merge_partials,
     unpack_mask_block,
+    unpack_mask_rows,
+    mask_block_of,
 )
 from .append_kv import (  # noqa: F401
     append_kv,

@@ -156,6 +156,36 @@ def unpack_mask_block(mask: np.ndarray, offset: int, L: int) -> np.ndarray:
     return block
 
 
+def unpack_mask_rows(mask: np.ndarray, offset: int, prefix: int, L: int) -> np.ndarray:
+    """Request's ``[L, L]`` bool draft block from sglang's full-row byte mask.
+
+    In that layout (flashmap page "sglang/verify_attention.py": module
+    docstring and the non-``QLEN_MASK`` branch of ``_verify_partial_kernel``)
+    request b's mask starts at byte ``offset = mask_indptr[b]`` and holds one
+    row of ``prefix + L`` bytes per query token, one byte per key, nonzero =
+    allowed. The prefix is all visible, so only the last ``L`` bytes of each
+    row are read: entry (t, j) is byte ``offset + t * (prefix + L) + prefix +
+    j``.
+    """
+    block = np.zeros((L, L), dtype=bool)
+    for t in range(L):
+        for j in range(L):
+            block[t, j] = int(mask[offset + t * (prefix + L) + prefix + j]) != 0
+    return block
+
+
+def mask_block_of(mask, mask_indptr, layout: str, b: int, prefix: int, L: int):
+    """The draft block of request b under ``layout`` ("bits" or "rows"), or
+    None without a mask (causal)."""
+    if mask is None:
+        return None
+    if layout == "bits":
+        return unpack_mask_block(mask, int(mask_indptr[b]), L)
+    if layout == "rows":
+        return unpack_mask_rows(mask, int(mask_indptr[b]), prefix, L)
+    raise ValueError(layout)
+
+
 def allowed_keys(L: int, prefix: int, kv_len: int, mask_block: Optional[np.ndarray]) -> np.ndarray:
     """``[L, kv_len]`` bool: which keys each of the request's query tokens sees."""
     allowed = np.zeros((L, kv_len), dtype=bool)
@@ -216,12 +246,13 @@ def _check_shapes(q, k_cache, v_cache, kv_indptr, last_page_len, qo_indptr, num_
 def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr,
                      mask=None, mask_indptr=None, *, sm_scale: float, k_scale: float = 1.0,
                      v_scale: float = 1.0, q_dtype: str, kv_dtype: str,
-                     requests: Optional[Sequence[int]] = None):
+                     requests: Optional[Sequence[int]] = None, mask_layout: str = "bits"):
     """The whole path on raw storage arrays; returns float64 ``out [T, Hq, D]``, ``lse [T, Hq]``.
 
-    ``mask=None`` means causal over the drafts; otherwise ``mask`` is the
-    bit-packed byte array and ``mask_indptr[b]`` the byte offset of request
-    b's ``L_b x L_b`` block. ``requests`` limits the work to some requests
+    ``mask=None`` means causal over the drafts. Otherwise, with
+    ``mask_layout="bits"``, ``mask`` is the bit-packed byte array and
+    ``mask_indptr[b]`` the byte offset of request b's ``L_b x L_b`` block;
+    with ``"rows"`` it is sglang's full-row byte mask (``unpack_mask_rows``). ``requests`` limits the work to some requests
     (rows of other requests stay 0 / -inf), for sampled checks at full size.
     Query head ``hq`` reads KV head ``hq // G`` (vLLM page "[Performance]
     Support MQA/GQA in prefill stage by using FlashAttention": K/V expanded
@@ -249,7 +280,7 @@ def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, 
         v_raw = gather_request_kv(v_cache, kv_indices, start, kv_len, page_size)
         k_req = decode_storage(k_raw, kv_dtype)
         v_req = decode_storage(v_raw, kv_dtype) * float(v_scale)
-        block = None if mask is None else unpack_mask_block(mask, int(mask_indptr[b]), L)
+        block = mask_block_of(mask, mask_indptr, mask_layout, b, prefix, L)
         allowed = allowed_keys(L, prefix, kv_len, block)
         t0 = int(qo_indptr[b])
         for hq in range(Hq):
@@ -267,7 +298,7 @@ def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, 
 def verify_attention_partials(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
                               qo_indptr, mask=None, mask_indptr=None, *, key_splits,
                               sm_scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
-                              q_dtype: str, kv_dtype: str):
+                              q_dtype: str, kv_dtype: str, mask_layout: str = "bits"):
     """Attention restricted to key ranges: one ``(out, lse)`` pair per range.
 
     ``key_splits(b, kv_len) -> list of (lo, hi)`` key ranges; each partial is
@@ -292,7 +323,7 @@ def verify_attention_partials(q, k_cache, v_cache, kv_indptr, kv_indices, last_p
                                kv_dtype)
         v_req = decode_storage(gather_request_kv(v_cache, kv_indices, start, kv_len, page_size),
                                kv_dtype) * float(v_scale)
-        block = None if mask is None else unpack_mask_block(mask, int(mask_indptr[b]), L)
+        block = mask_block_of(mask, mask_indptr, mask_layout, b, prefix, L)
         allowed = allowed_keys(L, prefix, kv_len, block)
         t0 = int(qo_indptr[b])
         parts = []

@@ -63,7 +63,8 @@ def oracle_of(p: Problem, requests=None):
     return verify_attention(p.q, p.k_cache, p.v_cache, p.kv_indptr, p.kv_indices,
                             p.last_page_len, p.qo_indptr, p.mask, p.mask_indptr,
                             sm_scale=p.sm_scale, k_scale=p.k_scale, v_scale=p.v_scale,
-                            q_dtype=p.q_dtype, kv_dtype=p.kv_dtype, requests=requests)
+                            q_dtype=p.q_dtype, kv_dtype=p.kv_dtype, requests=requests,
+                            mask_layout=p.mask_layout)
 
 
 def rows_of(p: Problem, requests):

@@ -126,7 +126,8 @@ def run_oracle(p: Problem, **kw):
     return verify_attention(p.q, p.k_cache, p.v_cache, p.kv_indptr, p.kv_indices,
                             p.last_page_len, p.qo_indptr, p.mask, p.mask_indptr,
                             sm_scale=p.sm_scale, k_scale=p.k_scale, v_scale=p.v_scale,
-                            q_dtype=p.q_dtype, kv_dtype=p.kv_dtype, **kw)
+                            q_dtype=p.q_dtype, kv_dtype=p.kv_dtype,
+                            mask_layout=p.mask_layout, **kw)
 
 
 def sdpa_reference(q_log, k_log, v_log, allowed_blocks, *, scale: float, v_scale: float = 1.0):

@@ -21,7 +21,10 @@ Bit-packed tree masks: request b's ``L_b x L_b`` block, row-major flat index
 ``mask_indptr[b] + i // 8``; 1 = token t may attend to draft j. The pages only
 show byte masks (flashmap page ``sglang/verify_attention.py``,
 ``_verify_partial_kernel``, the ``USE_MASK`` branch); this packing is the
-build's own layout.
+build's own layout. The same blocks can also be laid out as sglang's
+full-row byte masks (``mask_layout="rows"``: per request ``L_b`` rows of
+``prefix_b + L_b`` bytes, one per key, nonzero = allowed, the prefix bytes
+set as sglang writes them), the layout the flashmap page's kernel reads.
 """
 
 from __future__ import annotations
@@ -75,6 +78,7 @@ class Problem:
     name: str = ""
     seed: int = 0
     info: dict = field(default_factory=dict)
+    mask_layout: str = "bits"  # "bits": packed L x L blocks; "rows": full byte rows
 
     @property
     def batch(self) -> int:
@@ -133,6 +137,48 @@ def pack_mask_rows(blocks: Sequence[np.ndarray], pad_bytes: int = 0):
         for i, bit in enumerate(flat):
             if bit:
                 seg[i // 8] |= np.uint8(1 << (i % 8))
+        segments.append(seg)
+        indptr.append(indptr[-1] + seg.size)
+    data = np.concatenate(segments) if segments else np.zeros(0, dtype=np.uint8)
+    if data.size == 0:
+        data = np.zeros(1, dtype=np.uint8)
+    return data, np.asarray(indptr, dtype=np.int32)
+
+
+def pack_mask_full_rows(blocks: Sequence[np.ndarray], prefixes: Sequence[int],
+                        prefix_fill="ones", true_values="ones", pad_bytes: int = 0,
+                        gen: Optional[torch.Generator] = None):
+    """Lay per-request ``[L_b, L_b]`` bool blocks out as full byte rows.
+
+    Request b's segment holds ``L_b`` rows of ``prefix_b + L_b`` bytes, row t
+    at byte ``t * (prefix_b + L_b)`` of the segment. The draft columns hold the
+    block (``true_values`` "ones": allowed = 1; "random": a random nonzero
+    byte); the prefix columns hold ``prefix_fill``: "ones" (all visible, as
+    sglang writes them), "zeros" or "random" bytes. ``pad_bytes`` zero bytes
+    follow every segment.
+    """
+    g = gen if gen is not None else torch.Generator().manual_seed(0)
+    segments = []
+    indptr = [0]
+    for blk, prefix in zip(blocks, prefixes):
+        blk = np.asarray(blk, dtype=bool)
+        L = blk.shape[0]
+        width = int(prefix) + L
+        seg = np.zeros(L * width + pad_bytes, dtype=np.uint8)
+        rows = seg[:L * width].reshape(L, width) if L else seg[:0].reshape(0, width)
+        if prefix_fill == "ones":
+            rows[:, :prefix] = 1
+        elif prefix_fill == "random":
+            rows[:, :prefix] = torch.randint(0, 256, (L, int(prefix)), generator=g).numpy()
+        elif prefix_fill != "zeros":
+            raise ValueError(prefix_fill)
+        if true_values == "ones":
+            vals = np.ones((L, L), dtype=np.uint8)
+        elif true_values == "random":
+            vals = torch.randint(1, 256, (L, L), generator=g).numpy().astype(np.uint8)
+        else:
+            raise ValueError(true_values)
+        rows[:, prefix:] = np.where(blk, vals, 0)
         segments.append(seg)
         indptr.append(indptr[-1] + seg.size)
     data = np.concatenate(segments) if segments else np.zeros(0, dtype=np.uint8)
@@ -200,13 +246,19 @@ def make_case(
     poison: bool = True,
     name: str = "",
     gen: Optional[torch.Generator] = None,
+    mask_layout: str = "bits",
+    rows_prefix_fill: str = "ones",
+    rows_true_values: str = "ones",
 ) -> Problem:
     """Build one seeded problem.
 
     ``mask_kind``: "causal" (no mask array), "chain" (packed chain mask, equal
     to causal), "tree" (random tree per request unless ``parents`` is given,
     ancestor-or-self), "random" (independent bits with ``mask_density``; rows
-    may be fully masked), "full" (every bit set).
+    may be fully masked), "full" (every bit set). ``mask_layout`` "bits"
+    packs the blocks; "rows" lays them out as full byte rows
+    (``pack_mask_full_rows`` with ``rows_prefix_fill`` / ``rows_true_values``),
+    drawn after every other input so the rest of the problem is the same.
     """
     if q_dtype not in DTYPES_Q or kv_dtype not in DTYPES_KV:
         raise ValueError((q_dtype, kv_dtype))
@@ -258,7 +310,10 @@ def make_case(
                 blocks.append(np.ones((L, L), dtype=bool))
             else:
                 raise ValueError(mask_kind)
-        mask, mask_indptr = pack_mask_rows(blocks, pad_bytes=mask_pad_bytes)
+        if mask_layout == "bits":
+            mask, mask_indptr = pack_mask_rows(blocks, pad_bytes=mask_pad_bytes)
+        elif mask_layout != "rows":
+            raise ValueError(mask_layout)
 
     T = int(qo_indptr[-1])
     q32 = torch.randn((T, num_qo_heads, head_dim), generator=g, dtype=torch.float32)
@@ -283,6 +338,9 @@ def make_case(
     if poison:
         poison_unused(k_cache, kv_dtype, kv_indptr, kv_indices, last_page_len)
         poison_unused(v_cache, kv_dtype, kv_indptr, kv_indices, last_page_len)
+    if mask_kind != "causal" and mask_layout == "rows":
+        mask, mask_indptr = pack_mask_full_rows(blocks, prefix_lens, rows_prefix_fill,
+                                                rows_true_values, mask_pad_bytes, g)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(head_dim)
     if max_qo_len is None:
@@ -298,6 +356,7 @@ def make_case(
         head_dim=head_dim, name=name, seed=int(seed),
         info={"prefix_lens": prefix_lens, "qo_lens": qo_lens, "kv_lens": kv_lens,
               "parents": tree_parents, "mask_kind": mask_kind},
+        mask_layout=mask_layout if mask is not None else "bits",
     )
 
 
