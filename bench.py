@@ -296,6 +296,9 @@ def main():
                     help="verify: the attention path; append: the draft K/V cache write")
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--prefix", type=int, default=4096, help="prefix length for config 3")
+    ap.add_argument("--mask-layout", default="bits", choices=["bits", "rows"],
+                    help="tree-mask layout for config 3: packed L x L bits or sglang's full "
+                         "byte rows")
     ap.add_argument("--copies", type=int, default=0,
                     help="page-pool copies rotated over the steps (0: enough for >= 1 GiB)")
     ap.add_argument("--chunk-keys", type=int, default=-1, help="planner override (-1: planner)")
@@ -336,7 +339,8 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "copies": args.steps}), flush=True)
         return
 
-    p = make_config(args.config, prefix=args.prefix)
+    extra = {"mask_layout": args.mask_layout} if args.config == 3 else {}
+    p = make_config(args.config, prefix=args.prefix, **extra)
     if args.op == "append":
         bench_append(args, p, dev)
         return
@@ -364,7 +368,8 @@ def main():
         call = binding.PreparedCall(
             base["q"], kc, vc, base["kv_indptr"], idx, base["last_page_len"], base["qo_indptr"],
             base["mask"], base["mask_indptr"], sm_scale=p.sm_scale, k_scale=p.k_scale,
-            v_scale=p.v_scale, max_qo_len=p.max_qo_len, chunk_keys=args.chunk_keys)
+            v_scale=p.v_scale, max_qo_len=p.max_qo_len, chunk_keys=args.chunk_keys,
+            mask_layout=p.mask_layout)
         batches.append(call)
     torch.cuda.synchronize()
 
@@ -482,7 +487,8 @@ def main():
         "vs_baseline": None,
         "dtype": {"f32": "f32", "bf16": "bf16"}[p.q_dtype] + ("+e4m3kv" if p.kv_dtype == "e4m3" else ""),
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[args.config].format(p=args.prefix),
+        "config": {"workload": WORKLOAD_NAMES[args.config].format(p=args.prefix) +
+                   (", sglang full-row byte mask" if p.mask_layout == "rows" else ""),
                    "batch": p.batch, "query_tokens": tokens, "kv_bytes": kvb,
                    "parallelism": "single GPU", "page_pool_copies": copies},
         "kv_read_gbps_step": round(kvb / (ms_per_step * 1e-3) / 1e9, 1),

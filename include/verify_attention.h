@@ -11,8 +11,8 @@
  * share a KV head: vLLM page "[Performance] Support MQA/GQA in prefill stage
  * by using FlashAttention"), to
  *   - every prefix key n < prefix_b = kv_len_b - L_b, and
- *   - draft key j (key prefix_b + j) iff j <= t (causal, no mask) or iff bit
- *     (t, j) of the request's bit-packed mask is set (a tree mask in place of
+ *   - draft key j (key prefix_b + j) iff j <= t (causal, no mask) or iff
+ *     entry (t, j) of the request's mask allows it (a tree mask in place of
  *     the causal one: FlashInfer page "How to implement a tree attention with
  *     flashinfer"),
  * and returns out = softmax(sm_scale * k_scale * q.K^T) . (v_scale * V) and
@@ -38,10 +38,18 @@
  * Separate Q and KV dtypes for decode" (begin_forward docstring):
  * kv_len_b = (pages_b - 1) * page_size + last_page_len[b].
  *
- * Mask packing (this library's layout): request b's L_b x L_b block,
- * row-major flat index i = t * L_b + j, bit (i % 8), least significant first,
- * of byte mask[mask_indptr[b] + i / 8]; 1 = allowed. Each segment must hold
- * at least ceil(L_b * L_b / 8) bytes.
+ * Mask layouts (has_mask selects one; both cover the drafts only, the prefix
+ * being always visible):
+ *   1 = packed blocks (this library's layout): request b's L_b x L_b block,
+ *       row-major flat index i = t * L_b + j, bit (i % 8), least significant
+ *       first, of byte mask[mask_indptr[b] + i / 8]; 1 = allowed. Each
+ *       segment must hold at least ceil(L_b * L_b / 8) bytes.
+ *   2 = full byte rows (sglang's layout, as the flashmap page
+ *       "sglang/verify_attention.py" reads it): request b holds L_b rows of
+ *       prefix_b + L_b bytes from byte mask_indptr[b], one byte per key;
+ *       entry (t, j) is byte mask_indptr[b] + t * (prefix_b + L_b) + prefix_b
+ *       + j, nonzero = allowed. The prefix bytes are not read. Each segment
+ *       must hold L_b * (prefix_b + L_b) bytes.
  *
  * Device-content contract (not checked on the host, which never reads device
  * memory): kv_indptr non-decreasing from 0 with kv_indptr[B] <=
@@ -97,8 +105,9 @@ typedef struct {
   int32_t max_qo_len;     /* host bound on every L_b; <= 64 when has_mask */
   int32_t q_dtype;        /* vat_dtype_t: F32 or BF16; out has this dtype */
   int32_t kv_dtype;       /* F32 (with F32 q), BF16 or FP8_E4M3FN (with BF16 q) */
-  int32_t has_mask;       /* 0: causal drafts (mask ignored); 1: bit-packed mask */
-  int32_t num_mask_bytes; /* size of mask when has_mask */
+  int32_t has_mask;       /* 0: causal drafts (mask ignored); 1: packed L x L bit
+                             blocks; 2: full byte rows (see the mask layouts) */
+  int32_t num_mask_bytes; /* size of mask when has_mask (>= 1) */
   int32_t num_cus;        /* compute units to plan for; 0 = query the current device */
   int32_t chunk_keys;     /* -1: planner; 0: no split (one work item per request,
                              KV head and row block writes out directly);

@@ -123,11 +123,14 @@ def make_problem(*, batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_
                  num_mask_bytes=0, num_cus=0, chunk_keys=-1) -> VatProblem:
     return VatProblem(batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_pages,
                       num_kv_indices, num_qo_tokens, max_qo_len, q_dtype, kv_dtype,
-                      int(bool(has_mask)), num_mask_bytes, num_cus, chunk_keys)
+                      int(has_mask), num_mask_bytes, num_cus, chunk_keys)
+
+
+MASK_LAYOUTS = {"bits": 1, "rows": 2}
 
 
 def problem_from_tensors(q, k_cache, kv_indptr, kv_indices, mask=None, max_qo_len=None,
-                         num_cus=0, chunk_keys=-1) -> VatProblem:
+                         num_cus=0, chunk_keys=-1, mask_layout="bits") -> VatProblem:
     if q.dim() != 3 or k_cache.dim() != 4:
         raise ValueError("q must be [T, Hq, D] and caches [pages, page_size, Hkv, D]")
     batch = kv_indptr.numel() - 1
@@ -140,7 +143,7 @@ def problem_from_tensors(q, k_cache, kv_indptr, kv_indices, mask=None, max_qo_le
         batch=batch, num_qo_heads=q.shape[1], num_kv_heads=k_cache.shape[2], head_dim=q.shape[2],
         page_size=k_cache.shape[1], num_pages=k_cache.shape[0], num_kv_indices=kv_indices.numel(),
         num_qo_tokens=T, max_qo_len=int(max_qo_len), q_dtype=_dtype_code(q),
-        kv_dtype=_dtype_code(k_cache), has_mask=mask is not None,
+        kv_dtype=_dtype_code(k_cache), has_mask=0 if mask is None else MASK_LAYOUTS[mask_layout],
         num_mask_bytes=0 if mask is None else mask.numel(), num_cus=num_cus,
         chunk_keys=chunk_keys)
 
@@ -183,7 +186,8 @@ def _check_tensors(q, k_cache, v_cache, idx):
 
 
 def _prepare(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr, mask,
-             mask_indptr, sm_scale, max_qo_len, out, lse, workspace, chunk_keys, num_cus):
+             mask_indptr, sm_scale, max_qo_len, out, lse, workspace, chunk_keys, num_cus,
+             mask_layout="bits"):
     import torch
 
     idx = [("kv_indptr", kv_indptr), ("kv_indices", kv_indices), ("last_page_len", last_page_len),
@@ -196,7 +200,8 @@ def _prepare(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indpt
         if t.dtype != want:
             raise ValueError(f"{name} must be {want}")
     problem = problem_from_tensors(q, k_cache, kv_indptr, kv_indices, mask, max_qo_len,
-                                   num_cus=num_cus, chunk_keys=chunk_keys)
+                                   num_cus=num_cus, chunk_keys=chunk_keys,
+                                   mask_layout=mask_layout)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[2])
     if out is None:
@@ -214,18 +219,20 @@ def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, 
                      mask=None, mask_indptr=None, sm_scale: Optional[float] = None,
                      k_scale: float = 1.0, v_scale: float = 1.0, max_qo_len: Optional[int] = None,
                      out=None, lse=None, workspace=None, chunk_keys: int = -1, num_cus: int = 0,
-                     stream=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+                     stream=None, mask_layout: str = "bits") -> Tuple["torch.Tensor", "torch.Tensor"]:
     """Multi-query verification attention over a paged KV cache; returns (out, lse).
 
     ``sm_scale`` defaults to ``head_dim ** -0.5``; ``max_qo_len`` defaults to
     the shape-only bound ``T - (B - 1)``; ``chunk_keys`` -1 lets the planner
     choose the prefix split, 0 forces one work item per request (direct
     output), a positive multiple of 16 forces that chunk length.
+    ``mask_layout``: "bits" (packed L x L blocks) or "rows" (sglang's full
+    byte rows).
     """
     lib = load()
     problem, sm, out, lse, workspace, ws_bytes = _prepare(
         q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr, mask, mask_indptr,
-        sm_scale, max_qo_len, out, lse, workspace, chunk_keys, num_cus)
+        sm_scale, max_qo_len, out, lse, workspace, chunk_keys, num_cus, mask_layout)
     st = lib.verify_attention(ctypes.byref(problem), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                               _ptr(kv_indptr), _ptr(kv_indices), _ptr(last_page_len),
                               _ptr(qo_indptr), _ptr(mask), _ptr(mask_indptr), sm, float(k_scale),
@@ -314,12 +321,12 @@ class PreparedCall:
     def __init__(self, q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr,
                  mask=None, mask_indptr=None, sm_scale=None, k_scale=1.0, v_scale=1.0,
                  max_qo_len=None, out=None, lse=None, workspace=None, chunk_keys=-1, num_cus=0,
-                 stream=None):
+                 stream=None, mask_layout="bits"):
         self.lib = load()
         (self.problem, self.sm, self.out, self.lse, self.workspace,
          self.ws_bytes) = _prepare(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
                                    qo_indptr, mask, mask_indptr, sm_scale, max_qo_len, out, lse,
-                                   workspace, chunk_keys, num_cus)
+                                   workspace, chunk_keys, num_cus, mask_layout)
         self.keep = (q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr, mask,
                      mask_indptr)
         self.k_scale = float(k_scale)

@@ -11,7 +11,8 @@
 
 namespace vat {
 const void* tile_kernel(int kv_dtype, int head_dim, int rt);
-const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int pair);
+const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int pair,
+                          int mask_mode);
 const void* merge_kernel(int q_is_f32, int head_dim);
 const void* append_kernel(int src_dtype, int cache_dtype, int pow2_scales, int units);
 }  // namespace vat
@@ -137,8 +138,8 @@ vat_status_t launch_partial(const vat_problem_t* p, const vat_plan_t& plan, cons
   a.num_ids = plan.num_chunk_ids;
   a.has_mask = p->has_mask;
   a.slices = plan.slices;
-  const void* fn = plan.kernel ? vat::stream_kernel(p->kv_dtype, p->head_dim, plan.row_tiles_per_wave, plan.dma_waves,
-                                              plan.waves_keys)
+  const void* fn = plan.kernel ? vat::stream_kernel(p->kv_dtype, p->head_dim, plan.row_tiles_per_wave,
+                                                    plan.dma_waves, plan.waves_keys, p->has_mask)
                                : vat::tile_kernel(p->kv_dtype, p->head_dim, plan.row_tiles_per_wave);
   if (plan.lds_bytes > 65536) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, plan.lds_bytes) !=

@@ -24,6 +24,9 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+__device__ __forceinline__ long long clampll(long long x, long long lo, long long hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -291,6 +294,20 @@ __device__ __forceinline__ unsigned long long load_mask_row(const uint8_t* mask,
   if (nbytes > 8)  // ninth byte (only when L + (bit0 & 7) > 64, so the shift is < 64)
     bits |= (unsigned long long)mask[clampi(seg + (bit0 >> 3) + 8, 0, last)] << (64 - (bit0 & 7));
   if (L < 64) bits &= (1ull << L) - 1ull;
+  return bits;
+}
+
+// Bits j = 0..L-1 of row t of the request's full byte rows (prefix + L
+// bytes per row from byte `seg`; the draft bytes are the last L; nonzero =
+// allowed).
+__device__ __forceinline__ unsigned long long load_mask_row_bytes(const uint8_t* mask,
+                                                                  int num_mask_bytes, int seg,
+                                                                  int t, int L, int prefix) {
+  const long long last = max(num_mask_bytes - 1, 0);
+  const long long byte0 = seg + (long long)t * (prefix + L) + prefix;
+  unsigned long long bits = 0;
+  for (int j = 0; j < L && j < 64; ++j)
+    bits |= (unsigned long long)(mask[clampll(byte0 + j, 0, last)] != 0) << j;
   return bits;
 }
 

@@ -34,8 +34,9 @@ vat_status_t validate_problem(const vat_problem_t* p) {
                        (p->q_dtype == VAT_BF16 && p->kv_dtype == VAT_BF16) ||
                        (p->q_dtype == VAT_BF16 && p->kv_dtype == VAT_FP8_E4M3FN);
   if (!pair_ok) return VAT_ERR_UNSUPPORTED;
-  if (p->has_mask != 0 && p->has_mask != 1) return VAT_ERR_SHAPE;
+  if (p->has_mask < 0 || p->has_mask > 2) return VAT_ERR_SHAPE;
   if (p->has_mask && p->max_qo_len > kMaxMaskedLen) return VAT_ERR_UNSUPPORTED;
+  if (p->has_mask && p->num_mask_bytes < 1) return VAT_ERR_SHAPE;
   if (p->chunk_keys < -1 || (p->chunk_keys > 0 && p->chunk_keys % kChunkQuantum))
     return VAT_ERR_SHAPE;
   if (p->batch > 0 && p->num_qo_tokens > 0 && p->num_pages < 1) return VAT_ERR_SHAPE;
@@ -105,7 +106,8 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   const bool stream = (p->kv_dtype != VAT_F32) && !(fp8 && p->head_dim == 64);
   int dw = 0;
   if (stream) {
-    const int64_t max_tiles = fp8 ? kStreamThreads / 64 : kStreamMaxTiles;
+    // fp8 and full byte-row masks keep one row tile per wave (registers).
+    const int64_t max_tiles = (fp8 || p->has_mask == 2) ? kStreamThreads / 64 : kStreamMaxTiles;
     const int64_t bt = tiles <= max_tiles ? tiles : max_tiles;  // tiles per row block
     rt = bt <= kStreamThreads / 64 ? 1 : 2;
     wr = int(cdiv(bt, rt));

@@ -413,20 +413,25 @@ __device__ __forceinline__ void fill_window(int* win, const PartialArgs& a, int 
 // One wave's rows of a segment: Q^T operand fragments and mask rows. The
 // loads are issued by fetch() and used only after the caller's wait, so no
 // load is left for the compiler to wait on where the stages are computed:
-// the mask bytes stay raw until finish().
-template <int KV, int D, int RT>
+// the mask bytes stay raw until finish(). The four lanes l, l ^ 16, l ^ 32,
+// l ^ 48 hold one row and split its mask bytes: packed blocks (mask mode 1)
+// take at most nine bytes from the row's first, three per lane; full byte
+// rows (mode 2, ROWS) one byte per draft, sixteen per lane -- registers that
+// only the ROWS instantiations (one row tile per wave) carry.
+template <int KV, int D, int RT, bool ROWS>
 struct RowSet {
+  static constexpr int kRaw = ROWS ? 16 : 3;
   int row_t[RT], row_g[RT];
   bool row_ok[RT];
   unsigned long long row_bits[RT];
   unsigned qf[RT][D / 8];
-  unsigned raw[RT][9];  // mask bytes from the row's first byte on
+  unsigned raw[RT][kRaw];  // this lane's share of the row's mask bytes
 
-  __device__ __forceinline__ void fetch(const PartialArgs& a, int q_start, int L, int mask_off,
-                                        int row0, int h, int lane) {
+  __device__ __forceinline__ void fetch(const PartialArgs& a, int q_start, int L, int prefix,
+                                        int mask_off, int row0, int h, int lane) {
     const int l16 = lane & 15, j4 = lane >> 4;
     const int R = a.group * L;
-    const int last = max(a.num_mask_bytes - 1, 0);
+    const long long last = max(a.num_mask_bytes - 1, 0);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int row = row0 + rt * 16 + l16;
@@ -446,34 +451,56 @@ struct RowSet {
         qf[rt][4 * ks + 2] = x.z;
         qf[rt][4 * ks + 3] = x.w;
       }
-      // Row t of the packed L x L block starts at bit t L; L <= 64 bits span
-      // at most nine bytes (indices clamped to the mask buffer).
-      if (a.has_mask) {
-        const int byte0 = mask_off + ((min(row_t[rt], L - 1) * L) >> 3);
+      const int t = min(row_t[rt], L - 1);
+      if constexpr (ROWS) {
+        // Draft j of row t: byte mask_off + t (prefix + L) + prefix + j.
+        const long long byte0 = mask_off + (long long)t * (prefix + L) + prefix + 16 * j4;
 #pragma unroll
-        for (int i = 0; i < 9; ++i) raw[rt][i] = a.mask[clampi(byte0 + i, 0, last)];
+        for (int i = 0; i < 16; ++i) raw[rt][i] = a.mask[clampll(byte0 + i, 0, last)];
+      } else if (a.has_mask) {
+        // Row t of the packed L x L block starts at bit t L; L <= 64 bits
+        // span at most nine bytes (indices clamped to the mask buffer).
+        const long long byte0 = mask_off + ((t * L) >> 3) + 3 * j4;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) raw[rt][i] = a.mask[j4 < 3 ? clampll(byte0 + i, 0, last) : 0];
       }
     }
   }
 
-  __device__ __forceinline__ void finish(int L, bool has_mask) {
+  __device__ __forceinline__ void finish(int L, int mask_mode, int lane) {
+    const int j4 = lane >> 4;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       if (!row_ok[rt]) {
 #pragma unroll
         for (int k = 0; k < D / 8; ++k) qf[rt][k] = 0u;
       }
-      row_bits[rt] = 0;
-      if (has_mask && row_ok[rt]) {
-        unsigned long long acc = 0;
+      // This lane's bits of the row, then the OR over its four lanes.
+      unsigned long long part = 0;
+      if constexpr (ROWS) {
 #pragma unroll
-        for (int i = 7; i >= 0; --i) acc = (acc << 8) | raw[rt][i];
-        const int sh = (row_t[rt] * L) & 7;
-        unsigned long long bits = acc >> sh;
-        if (sh) bits |= (unsigned long long)raw[rt][8] << (64 - sh);
-        if (L < 64) bits &= (1ull << L) - 1ull;
-        row_bits[rt] = bits;
+        for (int i = 0; i < 16; ++i)
+          part |= (unsigned long long)((raw[rt][i] & 0xffu) != 0u) << (16 * j4 + i);
+      } else if (mask_mode) {
+        const int sh = (min(row_t[rt], L - 1) * L) & 7;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          const int kb = 3 * j4 + i;  // byte of the row's span
+          const int pos = 8 * kb - sh;
+          const unsigned long long b = j4 < 3 ? (unsigned long long)(raw[rt][i] & 0xffu) : 0ull;
+          part |= pos < 0 ? (b >> sh) : (pos < 64 ? (b << pos) : 0ull);
+        }
       }
+      if (mask_mode != 0) {
+        unsigned lo = (unsigned)part, hi = (unsigned)(part >> 32);
+        lo |= __shfl_xor(lo, 16);
+        hi |= __shfl_xor(hi, 16);
+        lo |= __shfl_xor(lo, 32);
+        hi |= __shfl_xor(hi, 32);
+        part = ((unsigned long long)hi << 32) | lo;
+        if (L < 64) part &= (1ull << L) - 1ull;
+      }
+      row_bits[rt] = row_ok[rt] ? part : 0ull;
     }
   }
 };
@@ -483,9 +510,9 @@ struct RowSet {
 // fp32 partial (v_scale not yet applied) and its base-2 log-sum-exp in slot
 // `slot`.
 // `rb`: row block; `row0`: this wave's first row within the block.
-template <int KV, int D, int RT>
+template <int KV, int D, int RT, bool ROWS>
 __device__ __forceinline__ void write_rows(const StreamAcc<D, RT>& acc, const float (&lrow)[RT],
-                                           const RowSet<KV, D, RT>& rs, const PartialArgs& a,
+                                           const RowSet<KV, D, RT, ROWS>& rs, const PartialArgs& a,
                                            int q_start, bool whole, int slot, int rb, int row0,
                                            int h, int lane) {
   constexpr int NDT = D / 16;
@@ -578,7 +605,7 @@ __device__ __forceinline__ void merge_pair_state(StreamAcc<D, RT>& acc, float (&
 // through one ring of LDS buffers filled by DMA. Wave w < waves_rows owns row
 // tiles [w RT, w RT + RT) of every segment and runs all of its keys, so no
 // two waves ever hold parts of the same row; all eight waves issue the DMA.
-template <int KV, int D, int RT, int NS, int DW, int P, int SK>
+template <int KV, int D, int RT, int NS, int DW, int P, int SK, bool ROWS>
 __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   using G = StreamGeom<KV, D, DW, SK>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -688,7 +715,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   const int row0 = tset * RT * 16;                  // within the row block
   const int rbase = rb * a.rows_per_block + row0;   // in the request's rows
   float* pair_slot = (float*)(smem + NS * G::STAGE + kStreamPageWindow * 4) + tset * PairSlot<D, RT>::FLOATS;
-  RowSet<KV, D, RT> rs;
+  RowSet<KV, D, RT, ROWS> rs;
   StreamAcc<D, RT> acc;
   Vis vis{0, 0, a.has_mask, 0};
   bool has_rows = false;
@@ -696,7 +723,8 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   auto start_segment = [&](int s) {
     seg_L = lane_val(sg.L, s);
     has_rows = rbase < a.group * seg_L;
-    rs.fetch(a, lane_val(sg.q_start, s), seg_L, lane_val(sg.mask_off, s), rbase, h, lane);
+    rs.fetch(a, lane_val(sg.q_start, s), seg_L, lane_val(sg.prefix, s), lane_val(sg.mask_off, s),
+             rbase, h, lane);
     vis.hi = lane_val(sg.hi, s);
     vis.masked_from = lane_val(sg.prefix, s);
     vis.t_min = rbase / a.group;
@@ -751,7 +779,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   } else {
     if (computes) wait_vmcnt<0>();
   }
-  if (computes) rs.finish(seg_L, a.has_mask);
+  if (computes) rs.finish(seg_L, a.has_mask, lane);
 
   // ---- the ring. Iteration g: DMA waves wait for their stage-g loads; the
   // barrier (everyone's have landed and every wave is done with stage g - 1);
@@ -768,7 +796,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
       // DMA when the wave issues any) and waited for.
       start_segment(s);
       wait_vmcnt<0>();
-      rs.finish(seg_L, a.has_mask);
+      rs.finish(seg_L, a.has_mask, lane);
     }
     if (g + NS - 1 < nst_all) issue(g + NS - 1, (g + NS - 1) % NS);
     if (computes && has_rows) {
@@ -789,7 +817,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
         for (int rt = 0; rt < RT; ++rt) lrow[rt] = rowsum4_v(acc.l[rt]);
       }
       if (computes && has_rows && phase == 0)
-        write_rows<KV, D, RT>(acc, lrow, rs, a, lane_val(sg.q_start, s), lane_val(sg.whole, s) != 0,
+        write_rows<KV, D, RT, ROWS>(acc, lrow, rs, a, lane_val(sg.q_start, s), lane_val(sg.whole, s) != 0,
                               lane_val(sg.slot, s), rb, row0, h, lane);
     }
   }
@@ -802,22 +830,32 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
 // 32 KB (64 bf16 keys of D = 128, else 128 keys); four of them fill the
 // 128 KB the planner gives the ring.
 template <int KV, int D, int NS, int SK>
-static const void* stream_variant(int rt, int dma_waves, int pair) {
+static const void* stream_variant(int rt, int dma_waves, int pair, bool rows) {
+  if (rows) {
+    // Full byte-row masks: one row tile per wave (the planner's choice).
+    if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK, true>;
+    if (dma_waves == 2) return (const void*)vat_stream<KV, D, 1, NS, 2, 1, SK, true>;
+    return pair == 2 ? (const void*)vat_stream<KV, D, 1, NS, 4, 2, SK, true>
+                     : (const void*)vat_stream<KV, D, 1, NS, 4, 1, SK, true>;
+  }
   if constexpr (KV != KV_E4M3)
-    if (rt == 2) return (const void*)vat_stream<KV, D, 2, NS, kSWaves, 1, SK>;
-  if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK>;
-  if (dma_waves == 2) return (const void*)vat_stream<KV, D, 1, NS, 2, 1, SK>;
-  return pair == 2 ? (const void*)vat_stream<KV, D, 1, NS, 4, 2, SK> : (const void*)vat_stream<KV, D, 1, NS, 4, 1, SK>;
+    if (rt == 2) return (const void*)vat_stream<KV, D, 2, NS, kSWaves, 1, SK, false>;
+  if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK, false>;
+  if (dma_waves == 2) return (const void*)vat_stream<KV, D, 1, NS, 2, 1, SK, false>;
+  return pair == 2 ? (const void*)vat_stream<KV, D, 1, NS, 4, 2, SK, false>
+                   : (const void*)vat_stream<KV, D, 1, NS, 4, 1, SK, false>;
 }
 
-const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int pair) {
+const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int pair,
+                          int mask_mode) {
   static_assert(stream_stage_keys(KV_BF16, 128) == 64 && stream_stage_keys(KV_BF16, 64) == 128 &&
                 stream_stage_keys(KV_E4M3, 128) == 128, "stage sizes match the planner");
+  const bool rows = mask_mode == 2;
   if (kv_dtype == KV_BF16)
-    return head_dim == 128 ? stream_variant<KV_BF16, 128, 4, 64>(rt, dma_waves, pair)
-                           : stream_variant<KV_BF16, 64, 4, 128>(rt, dma_waves, pair);
+    return head_dim == 128 ? stream_variant<KV_BF16, 128, 4, 64>(rt, dma_waves, pair, rows)
+                           : stream_variant<KV_BF16, 64, 4, 128>(rt, dma_waves, pair, rows);
   // The planner keeps fp8 at one row tile per wave.
-  return stream_variant<KV_E4M3, 128, 4, 128>(1, dma_waves, pair);
+  return stream_variant<KV_E4M3, 128, 4, 128>(1, dma_waves, pair, rows);
 }
 
 }  // namespace vat

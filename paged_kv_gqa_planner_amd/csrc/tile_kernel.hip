@@ -438,8 +438,11 @@ __global__ __launch_bounds__(kThreads) void vat_partial(PartialArgs a) {
     row_g[rt] = row % a.group;
     row_ok[rt] = row < R;
     row_bits[rt] = 0;
-    if (a.has_mask && row_ok[rt])
+    if (a.has_mask == 1 && row_ok[rt])
       row_bits[rt] = load_mask_row(a.mask, a.num_mask_bytes, r.mask_off, row_t[rt], r.L);
+    else if (a.has_mask == 2 && row_ok[rt])
+      row_bits[rt] = load_mask_row_bytes(a.mask, a.num_mask_bytes, r.mask_off, row_t[rt], r.L,
+                                         r.prefix);
   }
 
   // Q^T operand fragments.

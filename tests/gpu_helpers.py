@@ -48,7 +48,7 @@ def run_gpu(lib, p: Problem, tensors=None, **kw):
     out, lse = lib.verify_attention(
         t["q"], t["k_cache"], t["v_cache"], t["kv_indptr"], t["kv_indices"], t["last_page_len"],
         t["qo_indptr"], t["mask"], t["mask_indptr"], sm_scale=p.sm_scale, k_scale=p.k_scale,
-        v_scale=p.v_scale, max_qo_len=p.max_qo_len, **kw)
+        v_scale=p.v_scale, max_qo_len=p.max_qo_len, mask_layout=p.mask_layout, **kw)
     torch.cuda.synchronize()
     return out, lse
 

@@ -114,6 +114,20 @@ def test_plan_is_shape_only_and_deterministic(lib):
     assert c["chunk_keys"] <= d["chunk_keys"]
 
 
+def test_full_row_masks_keep_one_row_tile_per_wave(lib):
+    """Byte-row masks (layout 2) plan row blocks of at most 128 rows: the
+    kernels that read them hold one 16-row tile per wave."""
+    for G, L in [(4, 64), (8, 40), (2, 17)]:
+        bits = B.vat_plan(base_problem(num_qo_heads=2 * G, max_qo_len=L, num_qo_tokens=2 * L,
+                                       has_mask=1, num_mask_bytes=1024))
+        rows = B.vat_plan(base_problem(num_qo_heads=2 * G, max_qo_len=L, num_qo_tokens=2 * L,
+                                       has_mask=2, num_mask_bytes=100000))
+        assert rows.row_tiles_per_wave == 1 and rows.rows_per_block <= 128
+        assert rows.rows_per_block * rows.row_blocks >= G * L
+        if G * L <= 128:
+            assert rows.as_dict() == bits.as_dict()
+
+
 def test_forced_chunk_and_direct(lib):
     assert B.vat_plan(base_problem(chunk_keys=0)).direct == 1
     p = B.vat_plan(base_problem(chunk_keys=48))
@@ -204,6 +218,9 @@ def test_slice_segments_cover_each_request_once():
     (dict(q_dtype=0, kv_dtype=1), 3),
     (dict(q_dtype=1, kv_dtype=0), 3),
     (dict(has_mask=1, max_qo_len=65, num_mask_bytes=600), 3),
+    (dict(has_mask=2, max_qo_len=65, num_mask_bytes=600), 3),
+    (dict(has_mask=3, num_mask_bytes=8), 2),
+    (dict(has_mask=1, num_mask_bytes=0), 2),
     (dict(chunk_keys=40), 2),
     (dict(chunk_keys=-2), 2),
     (dict(batch=-1), 2),

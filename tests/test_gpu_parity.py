@@ -41,7 +41,7 @@ def test_config_parity(gpu_lib, cid, prefix):
 def _problem(lib, p, **kw):
     t = to_device(p)
     return lib.problem_from_tensors(t["q"], t["k_cache"], t["kv_indptr"], t["kv_indices"],
-                                    t["mask"], p.max_qo_len, **kw)
+                                    t["mask"], p.max_qo_len, mask_layout=p.mask_layout, **kw)
 
 
 # ---------------------------------------------------------------- seeded small-shape fuzz
