@@ -109,6 +109,19 @@ def timed_oracle(p, min_seconds: float, requests=None):
     return ref, (time.perf_counter() - t0), reps
 
 
+def profiled_traffic(key: str, src_hash: str):
+    """HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE) recorded in
+    profiles/traffic.json for this workload, or None when the record is
+    missing or was taken on different kernel sources."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    with open(PROFILE_TRAFFIC) as f:
+        entry = json.load(f).get(key)
+    if entry and entry.get("source_hash") == src_hash:
+        return entry.get("bytes_per_launch")
+    return None
+
+
 def append_source_hash() -> str:
     h = hashlib.sha256()
     for name in ("device_common.h", "append_kernel.hip", "plan.h", "api.hip"):
@@ -271,7 +284,8 @@ def bench_append(args, p, dev):
                    "source_copies": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "kernel": "vat_append",
+                     "traffic": profiled_traffic(f"append:{args.config}", append_source_hash()),
+                     "kernel": "vat_append",
                      "algorithmic_bytes_per_launch": alg_bytes},
         "verified": verified,
         "gpu_ran_ahead_of_host": bool(ahead),
@@ -462,14 +476,9 @@ def main():
         achieved = kvb / (part_avg * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4)}
-    roof["traffic"] = None
     src_hash = kernel_source_hash()
-    if os.path.exists(PROFILE_TRAFFIC):
-        with open(PROFILE_TRAFFIC) as f:
-            tr = json.load(f)
-        entry = tr.get(str(args.config) if args.config != 3 else f"3@{args.prefix}")
-        if entry and entry.get("source_hash") == src_hash:
-            roof["traffic"] = entry.get("bytes_per_launch")
+    key = str(args.config) if args.config != 3 else f"3@{args.prefix}"
+    roof["traffic"] = profiled_traffic(key if p.mask_layout == "bits" else key + ":rows", src_hash)
     roof["kernel"] = "vat_stream" if plan["kernel"] == 1 else "vat_tile"
     roof["algorithmic_bytes_per_launch"] = kvb
     roof["algorithmic_flops_per_launch"] = flops
