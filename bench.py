@@ -36,6 +36,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -57,13 +58,23 @@ WORKLOAD_NAMES = {
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash() -> str:
+def _code_hash(names) -> str:
+    """sha256 (first 16 hex) of the code of these csrc files with comments
+    and blank space removed, so a comment edit keeps recorded profiles valid
+    while any change to the code invalidates them."""
     h = hashlib.sha256()
-    for name in ("device_common.h", "stream_kernel.hip", "tile_kernel.hip", "merge_kernel.hip",
-                 "plan.cpp", "plan.h", "api.hip"):
-        with open(os.path.join(ROOT, "paged_kv_gqa_planner_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    for name in names:
+        with open(os.path.join(ROOT, "paged_kv_gqa_planner_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+def kernel_source_hash() -> str:
+    return _code_hash(("device_common.h", "stream_kernel.hip", "tile_kernel.hip",
+                       "merge_kernel.hip", "plan.cpp", "plan.h", "api.hip"))
 
 
 def algorithmic_work(p):
@@ -123,11 +134,7 @@ def profiled_traffic(key: str, src_hash: str):
 
 
 def append_source_hash() -> str:
-    h = hashlib.sha256()
-    for name in ("device_common.h", "append_kernel.hip", "plan.h", "api.hip"):
-        with open(os.path.join(ROOT, "paged_kv_gqa_planner_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    return _code_hash(("device_common.h", "append_kernel.hip", "plan.h", "api.hip"))
 
 
 def hold_stream_timer(torch, K, launches, host_per_launch):

@@ -119,10 +119,12 @@ typedef struct {
 typedef struct {
   int32_t direct;           /* 1: every request fits one chunk: no merge kernel,
                                the partial kernel writes out/lse itself */
-  int32_t kernel;           /* 1: LDS-ring streaming kernel (bf16/fp8 KV, at most
-                               256 (bf16) or 128 (fp8) query rows per KV head);
-                               0: row-tiled kernel */
-  int32_t stages;           /* streaming kernel: 64-key stages in flight in LDS */
+  int32_t kernel;           /* 1: LDS-ring streaming kernel (bf16 KV, and fp8 KV
+                               with D 128; rows in blocks of up to 256 (bf16) or
+                               128 (fp8, or full byte-row masks) per KV head);
+                               0: row-tiled kernel (fp32 KV, fp8 KV with D 64) */
+  int32_t stages;           /* streaming kernel: 32 KB stages in flight in LDS
+                               (64 keys at bf16 D 128, else 128 keys) */
   int32_t slices;           /* > 0: balanced scheduling. Per KV head, the page-index
                                space [0, num_kv_indices) is cut into `slices` equal
                                ranges, one workgroup each, which processes the
@@ -134,7 +136,7 @@ typedef struct {
   int32_t waves_rows;       /* waves splitting a row block's rows */
   int32_t waves_keys;       /* waves splitting each key range (streaming kernel:
                                waves per row tile set, each taking a share of
-                               every 64-key stage) */
+                               every stage's keys) */
   int32_t dma_waves;        /* streaming kernel: waves issuing the K/V loads (the
                                last dma_waves of eight) */
   int32_t rows_per_block;   /* M = waves_rows * row_tiles_per_wave * 16 */
