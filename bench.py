@@ -54,6 +54,8 @@ WORKLOAD_NAMES = {
     3: "tree verify bf16 at batch 1: Hq32 Hkv8 D128, L17 random tree, prefix {p}, page 16",
     4: "GQA causal prefill bf16: B10 x 1024 packed, Hq64 Hkv8 D128, page 16",
     5: "bf16 Q + fp8 e4m3 KV dynamic-draft verify: B64 Hq32 Hkv8 D128, prefix U[512,8192], L U{{1..8}}, page 16",
+    6: "GQA decode bf16: B64 Hq32 Hkv8 D128, prefix U[512,8192], L1, page 16",
+    7: "wide tree verify bf16: B4 Hq64 Hkv8 D128, L64 random tree (512 rows per KV head), prefix 8192, page 16",
 }
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -315,7 +317,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--op", default="verify", choices=["verify", "append"],
                     help="verify: the attention path; append: the draft K/V cache write")
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--prefix", type=int, default=4096, help="prefix length for config 3")
     ap.add_argument("--mask-layout", default="bits", choices=["bits", "rows"],
                     help="tree-mask layout for config 3: packed L x L bits or sglang's full "
@@ -395,7 +397,7 @@ def main():
     torch.cuda.synchronize()
 
     # ---- verification: copy 0 against the oracle, the others bitwise against copy 0
-    sample_requests = None if args.config != 4 else [0, p.batch - 1]
+    sample_requests = [0, p.batch - 1] if args.config in (4, 7) else None
     cpu = None
     if not args.no_cpu_baseline:
         ref, cpu_s, cpu_reps = timed_oracle(p, args.cpu_seconds, sample_requests)
@@ -475,7 +477,10 @@ def main():
     value = tokens * K / (total_ms * 1e-3)
     part_avg = partial_total_ms / K
     plan = batches[0].plan.as_dict()
-    if args.config == 4:
+    # The bound the workload's arithmetic intensity selects: above the ridge
+    # (bf16 MFMA peak / HBM peak, about 312 FLOP per KV byte) the MFMA units
+    # bound the kernel (the prefill and the wide trees), below it HBM does.
+    if flops / kvb > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
         achieved = flops / (part_avg * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}

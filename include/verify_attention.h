@@ -151,6 +151,10 @@ typedef struct {
   int32_t merge_threads;
   int32_t num_cus;          /* compute units planned for */
   int64_t workspace_bytes;  /* bytes of workspace the call needs (0 when direct) */
+  int32_t block_order;      /* 0: partial grid (num_chunk_ids, Hkv * row_blocks);
+                               1 (streaming kernel, more than one row block):
+                               one-dimensional grid in which the row blocks of
+                               each (work item, KV head) run on one XCD */
 } vat_plan_t;
 
 /* Plan a call: validates the shapes and fills *plan. Host only; touches the

@@ -138,6 +138,7 @@ vat_status_t launch_partial(const vat_problem_t* p, const vat_plan_t& plan, cons
   a.num_ids = plan.num_chunk_ids;
   a.has_mask = p->has_mask;
   a.slices = plan.slices;
+  a.block_order = plan.block_order;
   const void* fn = plan.kernel ? vat::stream_kernel(p->kv_dtype, p->head_dim, plan.row_tiles_per_wave,
                                                     plan.dma_waves, plan.waves_keys, p->has_mask)
                                : vat::tile_kernel(p->kv_dtype, p->head_dim, plan.row_tiles_per_wave);
@@ -333,6 +334,6 @@ const char* vat_status_string(vat_status_t status) {
   return "unknown status";
 }
 
-int32_t vat_abi_version(void) { return 1; }
+int32_t vat_abi_version(void) { return 2; }
 
 }  // extern "C"

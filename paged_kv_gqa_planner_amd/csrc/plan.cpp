@@ -232,6 +232,16 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   plan->num_chunk_ids = int32_t(ids);
   plan->grid_x = int32_t(ids);
   plan->grid_y = int32_t(p->num_kv_heads * RB);
+  if (stream && RB > 1) {
+    // Row blocks re-read their group's keys: keep each group's blocks on one
+    // XCD (one L2), eight groups per round (one-dimensional grid).
+    const int64_t groups = ids * p->num_kv_heads;
+    const int64_t g1 = 8 * RB * cdiv(groups, 8);
+    if (g1 > int64_t(INT32_MAX)) return VAT_ERR_UNSUPPORTED;
+    plan->block_order = 1;
+    plan->grid_x = int32_t(g1);
+    plan->grid_y = 1;
+  }
   if (direct) {
     plan->merge_grid = 0;
     plan->workspace_bytes = 0;

@@ -64,6 +64,7 @@ struct PartialArgs {
   int32_t rows_per_block, row_blocks, waves_rows, waves_keys;
   int32_t chunk_keys, num_ids, has_mask;
   int32_t slices;  // > 0: balanced page slices per KV head (streaming kernel, B <= 64)
+  int32_t block_order;  // 1: one-dimensional grid, row blocks of a group on one XCD
 };
 
 // Arguments of the merge kernel.

@@ -613,9 +613,23 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   // Row blocks of one KV head are dispatched longest first (under a causal
-  // limit a later block reaches more keys).
-  const int h = blockIdx.y / a.row_blocks;
-  const int rb = a.row_blocks - 1 - (int)(blockIdx.y % a.row_blocks);
+  // limit a later block reaches more keys). In block order 1 the grid is one-
+  // dimensional: workgroup L runs on XCD L % 8, and the row blocks of group
+  // q = (work item, KV head) take workgroups (q % 8) + 8 (RB (q / 8) + r), so
+  // they share that XCD's L2 and start within one round of eight groups.
+  int item, h, rb;
+  if (a.block_order) {
+    const int L = (int)blockIdx.x;
+    const int q = (L & 7) + 8 * (L / (8 * a.row_blocks));
+    if (q >= a.num_ids * a.hkv) return;
+    item = q % a.num_ids;
+    h = q / a.num_ids;
+    rb = a.row_blocks - 1 - (L >> 3) % a.row_blocks;
+  } else {
+    item = (int)blockIdx.x;
+    h = blockIdx.y / a.row_blocks;
+    rb = a.row_blocks - 1 - (int)(blockIdx.y % a.row_blocks);
+  }
   const int shift = a.page_shift;
 
   // ---- the segment lanes and the page window: one round of loads for a slice
@@ -623,7 +637,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   int w0, wcount;  // window range: kv_indices positions [w0, w0 + wcount)
   if (a.slices > 0) {
     const int per = (a.num_kv_indices + a.slices - 1) / a.slices;
-    w0 = blockIdx.x * per;
+    w0 = item * per;
     wcount = min(per, a.num_kv_indices - w0);
     if (wcount <= 0) return;
     // Page ids of the slice, requested with the request table below.
@@ -650,7 +664,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
       sg.L = r.L;
       sg.prefix = r.prefix;
       sg.mask_off = r.mask_off;
-      sg.slot = blockIdx.x + lane;
+      sg.slot = item + lane;
       sg.whole = sg.lo == 0 && sg.hi == r.kv_len;
     }
 #pragma unroll
@@ -659,12 +673,12 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
       if (i2 < min(wcount, kStreamPageWindow)) win[i2] = clampi(pid[k], 0, a.num_pages - 1);
     }
   } else {
-    // Chunk j of the request owning work item blockIdx.x: one segment (lane 0).
+    // Chunk j of the request owning work item `item`: one segment (lane 0).
     ReqArrays ra{a.kv_indptr, a.last_page_len, a.qo_indptr, a.has_mask ? a.mask_indptr : nullptr,
                  a.batch, shift, a.chunk_keys, a.num_kv_indices, a.tokens};
     Req r;
     Item it;
-    if (!find_item(ra, blockIdx.x, lane, r, it) || r.L == 0) return;
+    if (!find_item(ra, item, lane, r, it) || r.L == 0) return;
     if (rb * a.rows_per_block >= a.group * r.L) return;  // no row of this block exists
     const int lo = it.j * a.chunk_keys;
     int hi = min(lo + a.chunk_keys, r.kv_len);

@@ -43,7 +43,7 @@ def test_library_exports_every_header_function(lib):
             "vat_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.vat_abi_version() == 1
+    assert lib.vat_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -72,14 +72,19 @@ def base_problem(**kw):
     return B.make_problem(**f)
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7])
 def test_plans_for_the_workloads(lib, cid):
     p = make_config(cid, prefix=32768 if cid == 3 else 4096)
     plan = B.vat_plan(problem_of(p))
     G = p.num_qo_heads // p.num_kv_heads
     assert plan.group == G and plan.rows == G * p.max_qo_len
     assert plan.rows_per_block * plan.row_blocks >= plan.rows
-    assert plan.grid_y == p.num_kv_heads * plan.row_blocks
+    if plan.block_order:
+        groups = plan.num_chunk_ids * p.num_kv_heads
+        assert plan.grid_y == 1
+        assert plan.grid_x == 8 * plan.row_blocks * -(-groups // 8)
+    else:
+        assert plan.grid_y == p.num_kv_heads * plan.row_blocks
     if plan.slices:
         # Balanced slices: one workgroup per (slice, KV head), CU-filling.
         assert plan.kernel == 1 and plan.chunk_keys == 0
@@ -96,6 +101,10 @@ def test_plans_for_the_workloads(lib, cid):
         # Prefill: the streaming kernel in row blocks of 256 rows, whole requests.
         assert plan.kernel == 1 and plan.direct == 1 and plan.workspace_bytes == 0
         assert plan.rows_per_block == 256 and plan.row_blocks == 32 and plan.slices == 0
+    elif cid == 7:
+        # Wide trees: 512 rows per KV head in two blocks, chunked prefixes.
+        assert plan.kernel == 1 and plan.rows_per_block == 256 and plan.row_blocks == 2
+        assert plan.slices == 0 and plan.block_order == 1
     else:
         assert plan.kernel == 1 and plan.threads == 512 and plan.slices > 0
     if not plan.direct:
@@ -134,6 +143,43 @@ def test_forced_chunk_and_direct(lib):
     assert p.chunk_keys == 48 and p.direct == 0
     assert B.vat_workspace_size(base_problem(chunk_keys=0)) == 0
     assert B.vat_workspace_size(base_problem(chunk_keys=48)) == p.workspace_bytes > 0
+
+
+def _decode_block(L, row_blocks, num_ids, hkv):
+    """Host restatement of the streaming kernel's one-dimensional block order:
+    (work item, KV head, row block) of workgroup L, or None for padding."""
+    q = (L & 7) + 8 * (L // (8 * row_blocks))
+    if q >= num_ids * hkv:
+        return None
+    return q % num_ids, q // num_ids, row_blocks - 1 - (L >> 3) % row_blocks
+
+
+@pytest.mark.parametrize("cid", [4, 7])
+def test_row_blocks_of_a_group_share_an_xcd(lib, cid):
+    """Workgroup L runs on XCD L % 8. Every (item, head, row block) is launched
+    once, the row blocks of one (item, head) sit on one XCD and are launched
+    within one round of 8 * row_blocks workgroups, the XCDs get equal shares
+    of groups (to one), and a group's longest row block comes first."""
+    p = make_config(cid)
+    plan = B.vat_plan(problem_of(p))
+    assert plan.block_order == 1 and plan.row_blocks > 1
+    seen = {}
+    for L in range(plan.grid_x):
+        d = _decode_block(L, plan.row_blocks, plan.num_chunk_ids, p.num_kv_heads)
+        if d is None:
+            continue
+        assert d not in seen
+        seen[d] = L
+    assert len(seen) == plan.num_chunk_ids * p.num_kv_heads * plan.row_blocks
+    per_xcd = [0] * 8
+    for item in range(plan.num_chunk_ids):
+        for h in range(p.num_kv_heads):
+            Ls = [seen[(item, h, rb)] for rb in range(plan.row_blocks)]
+            assert len({L % 8 for L in Ls}) == 1
+            assert max(Ls) // (8 * plan.row_blocks) == min(Ls) // (8 * plan.row_blocks)
+            assert seen[(item, h, plan.row_blocks - 1)] == min(Ls)
+            per_xcd[Ls[0] % 8] += 1
+    assert max(per_xcd) - min(per_xcd) <= 1
 
 
 def test_chunk_ids_of_consecutive_requests_are_disjoint():

@@ -20,7 +20,8 @@ pytestmark = pytest.mark.gpu
 # ---------------------------------------------------------------- the five workloads
 
 
-CONFIG_CASES = [(1, None), (2, None), (3, 4096), (3, 16384), (3, 32768), (4, None), (5, None)]
+CONFIG_CASES = [(1, None), (2, None), (3, 4096), (3, 16384), (3, 32768), (4, None), (5, None),
+                (6, None), (7, None)]
 
 
 @pytest.mark.parametrize("cid,prefix", CONFIG_CASES, ids=lambda x: str(x))
@@ -31,7 +32,7 @@ def test_config_parity(gpu_lib, cid, prefix):
     say(f"  plan {plan}")
     out, lse = run_gpu(gpu_lib, p)
     got_o, got_l = to_f64(out, lse)
-    requests = None if cid != 4 else [0, 9]
+    requests = {4: [0, 9], 7: [0, 3]}.get(cid)
     ref_o, ref_l = oracle_of(p, requests=requests)
     rows = None if requests is None else rows_of(p, requests)
     eo, el = compare(p, got_o, got_l, ref_o, ref_l, rows=rows, what=f"config {cid}")

@@ -51,6 +51,8 @@ CONFIG_NAMES = {
     3: "tree verify bf16 at batch 1 (Hq32 Hkv8 D128, L17 tree, prefix {p})",
     4: "GQA causal prefill bf16 (B10x1024, Hq64 Hkv8 D128)",
     5: "mixed-dtype dynamic-draft verify (B64 Hq32 Hkv8 D128, bf16 Q, e4m3 KV, prefix U[512,8192], L U{{1..8}})",
+    6: "GQA decode bf16 (B64 Hq32 Hkv8 D128, prefix U[512,8192], L1)",
+    7: "wide tree verify bf16 (B4 Hq64 Hkv8 D128, L64 tree, prefix 8192: 512 rows per KV head)",
 }
 
 
@@ -376,6 +378,11 @@ def make_config(cid: int, seed: Optional[int] = None, prefix: int = 4096, **over
        Hkv 8, D 128, prefix 0, K/V in the paged cache.
     5: bf16 Q with e4m3fn K/V (per-tensor absmax/448 scales), B 64, Hq 32,
        Hkv 8, D 128, prefix U[512, 8192], L U{1..8} causal, max_qo_len 8.
+    6: pure decode, bf16, B 64, Hq 32, Hkv 8, D 128, prefix U[512, 8192]
+       (config 5's length mix), one query token per request.
+    7: wide trees, bf16, B 4, Hq 64, Hkv 8, D 128, L 64 (random tree,
+       ancestor-or-self mask), prefix 8192: G L = 512 query rows per
+       (request, KV head), more than one row block.
     """
     seed = cid if seed is None else seed
     if cid == 1:
@@ -398,6 +405,14 @@ def make_config(cid: int, seed: Optional[int] = None, prefix: int = 4096, **over
         kw = dict(prefix_lens=prefixes, qo_lens=lens, num_qo_heads=32, num_kv_heads=8,
                   head_dim=128, q_dtype="bf16", kv_dtype="e4m3", fp8_absmax_scales=True,
                   max_qo_len=8, gen=g)
+    elif cid == 6:
+        g = torch.Generator().manual_seed(int(seed))
+        prefixes = torch.randint(512, 8193, (64,), generator=g).tolist()
+        kw = dict(prefix_lens=prefixes, qo_lens=[1] * 64, num_qo_heads=32, num_kv_heads=8,
+                  head_dim=128, gen=g)
+    elif cid == 7:
+        kw = dict(prefix_lens=[8192] * 4, qo_lens=[64] * 4, num_qo_heads=64, num_kv_heads=8,
+                  head_dim=128, mask_kind="tree")
     else:
         raise ValueError(cid)
     kw.update(overrides)
