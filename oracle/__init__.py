@@ -39,3 +39,4 @@ from .append_kv import (  # noqa: F401
     round_to_f32,
     source_values,
 )
+from .rope import rotate as rope_rotate, rotate_f32 as rope_rotate_f32  # noqa: F401

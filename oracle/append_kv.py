@@ -38,7 +38,7 @@ Everything else in the cache is left untouched.
 
 from __future__ import annotations
 
-from typing import Tuple
+from typing import Optional, Tuple
 
 import numpy as np
 
@@ -158,17 +158,24 @@ def source_values(raw: np.ndarray, src_dtype: str) -> np.ndarray:
 
 def append_kv(k_new, v_new, src_dtype: str, k_cache, v_cache, cache_dtype: str,
               kv_indptr, kv_indices, last_page_len, qo_indptr, page_size: int,
-              k_scale: float = 1.0, v_scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
+              k_scale: float = 1.0, v_scale: float = 1.0,
+              k_cos_sin: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Caches after writing each request's draft keys/values; inputs unchanged.
 
     ``k_new``/``v_new``: ``[T, Hkv, D]`` raw arrays in ``src_dtype``, rows in the
     packed ``qo_indptr`` order; caches ``[pages, page_size, Hkv, D]`` raw arrays
-    in ``cache_dtype``.
+    in ``cache_dtype``. ``k_cos_sin [T, D]``: rotate key row t by RoPE in
+    binary32 (``oracle.rope.rotate_f32``) before it is scaled and rounded;
+    values are written as given.
     """
     k_out = np.array(k_cache, copy=True)
     v_out = np.array(v_cache, copy=True)
     kx = source_values(k_new, src_dtype)
     vx = source_values(v_new, src_dtype)
+    if k_cos_sin is not None:
+        from .rope import rotate_f32
+
+        kx = rotate_f32(kx, np.asarray(k_cos_sin, dtype=np.float32)[:, None, :])
     num_pages = k_out.shape[0]
     for b in range(len(qo_indptr) - 1):
         pages, kv_len, L, prefix = request_lengths(kv_indptr, last_page_len, qo_indptr,

@@ -246,13 +246,17 @@ def _check_shapes(q, k_cache, v_cache, kv_indptr, last_page_len, qo_indptr, num_
 def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr,
                      mask=None, mask_indptr=None, *, sm_scale: float, k_scale: float = 1.0,
                      v_scale: float = 1.0, q_dtype: str, kv_dtype: str,
-                     requests: Optional[Sequence[int]] = None, mask_layout: str = "bits"):
+                     requests: Optional[Sequence[int]] = None, mask_layout: str = "bits",
+                     q_cos_sin: Optional[np.ndarray] = None):
     """The whole path on raw storage arrays; returns float64 ``out [T, Hq, D]``, ``lse [T, Hq]``.
 
     ``mask=None`` means causal over the drafts. Otherwise, with
     ``mask_layout="bits"``, ``mask`` is the bit-packed byte array and
     ``mask_indptr[b]`` the byte offset of request b's ``L_b x L_b`` block;
-    with ``"rows"`` it is sglang's full-row byte mask (``unpack_mask_rows``). ``requests`` limits the work to some requests
+    with ``"rows"`` it is sglang's full-row byte mask (``unpack_mask_rows``).
+    ``q_cos_sin [T, D]``: rotate query row t by RoPE with its cos/sin row
+    (``oracle.rope.rotate``, float64) before attending; the cached keys are
+    used as stored (a writer that applies RoPE stores rotated keys). ``requests`` limits the work to some requests
     (rows of other requests stay 0 / -inf), for sampled checks at full size.
     Query head ``hq`` reads KV head ``hq // G`` (vLLM page "[Performance]
     Support MQA/GQA in prefill stage by using FlashAttention": K/V expanded
@@ -266,6 +270,10 @@ def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, 
     G = Hq // num_kv_heads
     page_size = k_cache.shape[1]
     qf = decode_storage(q, q_dtype)
+    if q_cos_sin is not None:
+        from .rope import rotate
+
+        qf = rotate(qf, np.asarray(q_cos_sin)[:, None, :])
     out = np.zeros((T, Hq, D), dtype=np.float64)
     lse = np.full((T, Hq), -np.inf, dtype=np.float64)
     logit_scale = float(sm_scale) * float(k_scale)

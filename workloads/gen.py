@@ -484,3 +484,40 @@ def make_append_inputs(p: Problem, src_dtype: str, seed: int, spread: float = 1.
         return (k32.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy(),
                 v32.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy())
     raise ValueError(src_dtype)
+
+
+# ---------------------------------------------------------------- rotary positions
+
+
+def tree_depths(parents: Sequence[int]) -> np.ndarray:
+    """Depth of each node of a draft tree (root 0), parents before children."""
+    d = np.zeros(len(parents), dtype=np.int64)
+    for i in range(1, len(parents)):
+        d[i] = d[int(parents[i])] + 1
+    return d
+
+
+def rope_positions(p: Problem) -> np.ndarray:
+    """Position of every query/draft token row: ``prefix_b`` plus its depth in
+    the request's tree (a chain, or no mask: its index t)."""
+    pos = np.zeros(p.num_tokens, dtype=np.int64)
+    parents = p.info.get("parents")
+    for b in range(p.batch):
+        r0, r1 = int(p.qo_indptr[b]), int(p.qo_indptr[b + 1])
+        L = r1 - r0
+        prefix = p.info["kv_lens"][b] - L
+        if parents is not None and parents[b] is not None and len(parents[b]) == L:
+            pos[r0:r1] = prefix + tree_depths(parents[b])
+        else:
+            pos[r0:r1] = prefix + np.arange(L)
+    return pos
+
+
+def rope_cos_sin(positions, head_dim: int, theta: float = 10000.0) -> np.ndarray:
+    """``[len(positions), D]`` float32 rows ``(cos th_0.., sin th_0..)`` with
+    ``th_i = position * theta ** (-2 i / D)`` (LLaMA-style RoPE), evaluated in
+    float64 and rounded once."""
+    pos = np.asarray(positions, dtype=np.float64)[:, None]
+    inv = theta ** (-2.0 * np.arange(head_dim // 2, dtype=np.float64) / head_dim)
+    th = pos * inv[None, :]
+    return np.concatenate([np.cos(th), np.sin(th)], axis=1).astype(np.float32)
