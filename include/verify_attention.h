@@ -112,6 +112,9 @@ typedef struct {
   int32_t chunk_keys;     /* -1: planner; 0: no split (one work item per request,
                              KV head and row block writes out directly);
                              > 0: chunk length in keys, multiple of 16 */
+  int32_t rope;           /* 0; 1: verify_attention_rope rotates the queries by
+                             RoPE (bf16 caches or fp8 with D 128; not with
+                             full byte-row masks) */
 } vat_problem_t;
 
 /* What the planner decided; filled by vat_plan. Shape-only: the same problem
@@ -179,6 +182,26 @@ vat_status_t verify_attention(const vat_problem_t* problem, const void* q, const
                               float v_scale, void* out, float* lse, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* verify_attention with rotary position embedding applied to the queries
+ * inside the partial kernel (FlashInfer page "feat: Separate Q and KV dtypes
+ * for decode": RoPE applied on the fly in the attention kernels; a draft tree
+ * needs it at each token's own position, FlashInfer page "How to implement a
+ * tree attention with flashinfer"). q_cos_sin: device float32 [T, D], 16-byte
+ * aligned; row r holds cos(th_0) .. cos(th_{D/2-1}), sin(th_0) ..
+ * sin(th_{D/2-1}) of query token r's position. Query row r is rotated LLaMA
+ * style -- dimension i pairs with i + D/2: q'_i = q_i c_i - q_{i+D/2} s_i,
+ * q'_{i+D/2} = q_{i+D/2} c_i + q_i s_i -- in float32 and rounded to bf16
+ * before the products. Cached keys are used as stored: a cache written with
+ * vat_append_kv_rope holds rotated keys. problem->rope must be 1. */
+vat_status_t verify_attention_rope(const vat_problem_t* problem, const void* q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* kv_indptr, const int32_t* kv_indices,
+                                   const int32_t* last_page_len, const int32_t* qo_indptr,
+                                   const uint8_t* mask, const int32_t* mask_indptr,
+                                   const float* q_cos_sin, float sm_scale, float k_scale,
+                                   float v_scale, void* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
 /* The two halves of verify_attention, for timing each kernel on its own
  * stream position. vat_launch_partial enqueues the partial kernel only (in a
  * direct plan it writes out and lse); vat_launch_merge enqueues the merge
@@ -227,6 +250,22 @@ vat_status_t vat_append_kv(const vat_problem_t* problem, int32_t src_dtype, cons
                            const int32_t* kv_indptr, const int32_t* kv_indices,
                            const int32_t* last_page_len, const int32_t* qo_indptr, float k_scale,
                            float v_scale, void* stream);
+
+/* vat_append_kv with the keys rotated by RoPE before they are scaled and
+ * rounded (values are written as given). k_cos_sin: device float32 [T, D],
+ * 16-byte aligned, row r = (cos th_i .., sin th_i ..) of draft row r's
+ * position, the layout of verify_attention_rope. The rotation is evaluated in
+ * binary32 with each product and each sum rounded on its own (no fused
+ * multiply-add): k'_i = RN(RN(k_i c_i) - RN(k_{i+D/2} s_i)), k'_{i+D/2} =
+ * RN(RN(k_{i+D/2} c_i) + RN(k_i s_i)); a NaN result (from a NaN input, or
+ * infinity times zero) is the canonical positive quiet NaN. The stored code
+ * of k' then follows the rules of vat_append_kv exactly. */
+vat_status_t vat_append_kv_rope(const vat_problem_t* problem, int32_t src_dtype,
+                                const void* k_new, const void* v_new, void* k_cache,
+                                void* v_cache, const int32_t* kv_indptr,
+                                const int32_t* kv_indices, const int32_t* last_page_len,
+                                const int32_t* qo_indptr, const float* k_cos_sin, float k_scale,
+                                float v_scale, void* stream);
 
 /* Static description of a status code. */
 const char* vat_status_string(vat_status_t status);

@@ -21,7 +21,8 @@ LLaMA style pairs dimension ``i`` with ``i + D/2`` (i < D/2):
 ``rotate`` evaluates this in float64 (the attention oracle). ``rotate_f32``
 evaluates it in IEEE binary32 with every product and sum rounded on its own
 (no fused multiply-add): that is how the cache write defines the rotated key
-it then rounds to the cache dtype, so the stored codes are reproducible.
+it then rounds to the cache dtype, so the stored codes are reproducible; a
+NaN it produces is the canonical positive quiet NaN.
 The cos/sin rows themselves are inputs (drawn by the input recipe from the
 tokens' positions).
 """
@@ -57,4 +58,9 @@ def rotate_f32(x: np.ndarray, cos_sin: np.ndarray) -> np.ndarray:
     with np.errstate(over="ignore", invalid="ignore"):
         new_lo = (lo * c).astype(np.float32) - (hi * s).astype(np.float32)
         new_hi = (hi * c).astype(np.float32) + (lo * s).astype(np.float32)
-    return np.concatenate([new_lo.astype(np.float32), new_hi.astype(np.float32)], axis=-1)
+    out = np.concatenate([new_lo.astype(np.float32), new_hi.astype(np.float32)], axis=-1)
+    # Any NaN result (a NaN input, or infinity times zero) is the canonical
+    # positive quiet NaN: the sign of an invalid result is platform-defined.
+    bits = out.view(np.uint32)
+    bits[np.isnan(out)] = np.uint32(0x7FC00000)
+    return out

@@ -28,7 +28,7 @@ class VatProblem(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "batch", "num_qo_heads", "num_kv_heads", "head_dim", "page_size", "num_pages",
         "num_kv_indices", "num_qo_tokens", "max_qo_len", "q_dtype", "kv_dtype", "has_mask",
-        "num_mask_bytes", "num_cus", "chunk_keys")]
+        "num_mask_bytes", "num_cus", "chunk_keys", "rope")]
 
 
 class VatPlan(ctypes.Structure):
@@ -77,6 +77,11 @@ def load(path: Optional[str] = None):
     lib.vat_launch_partial.argtypes = full
     lib.vat_launch_partial.restype = ctypes.c_int
     lib.vat_launch_merge.argtypes = [P(VatProblem), vp, vp, vp, f, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.verify_attention_rope.argtypes = full[:10] + [vp] + full[10:]
+    lib.verify_attention_rope.restype = ctypes.c_int
+    lib.vat_append_kv_rope.argtypes = [P(VatProblem), ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp,
+                                       vp, vp, f, f, vp]
+    lib.vat_append_kv_rope.restype = ctypes.c_int
     lib.vat_launch_merge.restype = ctypes.c_int
     lib.vat_append_kv.argtypes = [P(VatProblem), ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp,
                                   f, f, vp]
@@ -120,17 +125,17 @@ def _dtype_code(t) -> int:
 
 def make_problem(*, batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_pages,
                  num_kv_indices, num_qo_tokens, max_qo_len, q_dtype, kv_dtype, has_mask,
-                 num_mask_bytes=0, num_cus=0, chunk_keys=-1) -> VatProblem:
+                 num_mask_bytes=0, num_cus=0, chunk_keys=-1, rope=0) -> VatProblem:
     return VatProblem(batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_pages,
                       num_kv_indices, num_qo_tokens, max_qo_len, q_dtype, kv_dtype,
-                      int(has_mask), num_mask_bytes, num_cus, chunk_keys)
+                      int(has_mask), num_mask_bytes, num_cus, chunk_keys, int(bool(rope)))
 
 
 MASK_LAYOUTS = {"bits": 1, "rows": 2}
 
 
 def problem_from_tensors(q, k_cache, kv_indptr, kv_indices, mask=None, max_qo_len=None,
-                         num_cus=0, chunk_keys=-1, mask_layout="bits") -> VatProblem:
+                         num_cus=0, chunk_keys=-1, mask_layout="bits", rope=False) -> VatProblem:
     if q.dim() != 3 or k_cache.dim() != 4:
         raise ValueError("q must be [T, Hq, D] and caches [pages, page_size, Hkv, D]")
     batch = kv_indptr.numel() - 1
@@ -145,7 +150,7 @@ def problem_from_tensors(q, k_cache, kv_indptr, kv_indices, mask=None, max_qo_le
         num_qo_tokens=T, max_qo_len=int(max_qo_len), q_dtype=_dtype_code(q),
         kv_dtype=_dtype_code(k_cache), has_mask=0 if mask is None else MASK_LAYOUTS[mask_layout],
         num_mask_bytes=0 if mask is None else mask.numel(), num_cus=num_cus,
-        chunk_keys=chunk_keys)
+        chunk_keys=chunk_keys, rope=rope)
 
 
 def vat_plan(problem: VatProblem) -> VatPlan:
@@ -187,7 +192,7 @@ def _check_tensors(q, k_cache, v_cache, idx):
 
 def _prepare(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr, mask,
              mask_indptr, sm_scale, max_qo_len, out, lse, workspace, chunk_keys, num_cus,
-             mask_layout="bits"):
+             mask_layout="bits", q_cos_sin=None):
     import torch
 
     idx = [("kv_indptr", kv_indptr), ("kv_indices", kv_indices), ("last_page_len", last_page_len),
@@ -199,9 +204,14 @@ def _prepare(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indpt
         want = torch.uint8 if name == "mask" else torch.int32
         if t.dtype != want:
             raise ValueError(f"{name} must be {want}")
+    if q_cos_sin is not None:
+        if not q_cos_sin.is_cuda or not q_cos_sin.is_contiguous() or q_cos_sin.dtype != torch.float32:
+            raise ValueError("q_cos_sin must be a contiguous float32 device tensor")
+        if tuple(q_cos_sin.shape) != (q.shape[0], q.shape[2]):
+            raise ValueError("q_cos_sin must be [T, D]")
     problem = problem_from_tensors(q, k_cache, kv_indptr, kv_indices, mask, max_qo_len,
                                    num_cus=num_cus, chunk_keys=chunk_keys,
-                                   mask_layout=mask_layout)
+                                   mask_layout=mask_layout, rope=q_cos_sin is not None)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[2])
     if out is None:
@@ -219,7 +229,8 @@ def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, 
                      mask=None, mask_indptr=None, sm_scale: Optional[float] = None,
                      k_scale: float = 1.0, v_scale: float = 1.0, max_qo_len: Optional[int] = None,
                      out=None, lse=None, workspace=None, chunk_keys: int = -1, num_cus: int = 0,
-                     stream=None, mask_layout: str = "bits") -> Tuple["torch.Tensor", "torch.Tensor"]:
+                     stream=None, mask_layout: str = "bits",
+                     q_cos_sin=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """Multi-query verification attention over a paged KV cache; returns (out, lse).
 
     ``sm_scale`` defaults to ``head_dim ** -0.5``; ``max_qo_len`` defaults to
@@ -227,17 +238,18 @@ def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, 
     choose the prefix split, 0 forces one work item per request (direct
     output), a positive multiple of 16 forces that chunk length.
     ``mask_layout``: "bits" (packed L x L blocks) or "rows" (sglang's full
-    byte rows).
+    byte rows). ``q_cos_sin`` ([T, D] float32 cos/sin rows of the query
+    tokens' positions) rotates the queries by RoPE inside the kernel.
     """
     lib = load()
     problem, sm, out, lse, workspace, ws_bytes = _prepare(
         q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr, mask, mask_indptr,
-        sm_scale, max_qo_len, out, lse, workspace, chunk_keys, num_cus, mask_layout)
-    st = lib.verify_attention(ctypes.byref(problem), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                              _ptr(kv_indptr), _ptr(kv_indices), _ptr(last_page_len),
-                              _ptr(qo_indptr), _ptr(mask), _ptr(mask_indptr), sm, float(k_scale),
-                              float(v_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
-                              _stream_handle(stream))
+        sm_scale, max_qo_len, out, lse, workspace, chunk_keys, num_cus, mask_layout, q_cos_sin)
+    st = lib.verify_attention_rope(ctypes.byref(problem), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(kv_indptr), _ptr(kv_indices), _ptr(last_page_len),
+                                   _ptr(qo_indptr), _ptr(mask), _ptr(mask_indptr),
+                                   _ptr(q_cos_sin), sm, float(k_scale), float(v_scale), _ptr(out),
+                                   _ptr(lse), _ptr(workspace), ws_bytes, _stream_handle(stream))
     _check(st, "verify_attention")
     return out, lse
 
@@ -260,7 +272,7 @@ def append_problem(k_new, k_cache, kv_indptr, kv_indices, max_qo_len=None,
 
 
 def _append_args(k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
-                 qo_indptr, k_scale, v_scale, max_qo_len, stream, num_cus=0):
+                 qo_indptr, k_scale, v_scale, max_qo_len, stream, num_cus=0, k_cos_sin=None):
     import torch
 
     idx = [("kv_indptr", kv_indptr), ("kv_indices", kv_indices),
@@ -274,24 +286,34 @@ def _append_args(k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices, last_pag
     if k_new.shape[1:] != k_cache.shape[2:]:
         raise ValueError("k_new rows must be [Hkv, D] of the cache")
     problem = append_problem(k_new, k_cache, kv_indptr, kv_indices, max_qo_len, num_cus)
-    return problem, (ctypes.byref(problem), _dtype_code(k_new), _ptr(k_new), _ptr(v_new),
-                     _ptr(k_cache), _ptr(v_cache), _ptr(kv_indptr), _ptr(kv_indices),
-                     _ptr(last_page_len), _ptr(qo_indptr), float(k_scale), float(v_scale),
-                     _stream_handle(stream))
+    head = (ctypes.byref(problem), _dtype_code(k_new), _ptr(k_new), _ptr(v_new),
+            _ptr(k_cache), _ptr(v_cache), _ptr(kv_indptr), _ptr(kv_indices),
+            _ptr(last_page_len), _ptr(qo_indptr))
+    tail = (float(k_scale), float(v_scale), _stream_handle(stream))
+    if k_cos_sin is None:
+        return problem, head + tail, False
+    if not k_cos_sin.is_cuda or not k_cos_sin.is_contiguous() or k_cos_sin.dtype != torch.float32:
+        raise ValueError("k_cos_sin must be a contiguous float32 device tensor")
+    if tuple(k_cos_sin.shape) != (k_new.shape[0], k_new.shape[2]):
+        raise ValueError("k_cos_sin must be [T, D]")
+    return problem, head + (_ptr(k_cos_sin),) + tail, True
 
 
 def append_kv(k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr,
               k_scale: float = 1.0, v_scale: float = 1.0, max_qo_len: Optional[int] = None,
-              stream=None, num_cus: int = 0):
+              stream=None, num_cus: int = 0, k_cos_sin=None):
     """Write the drafts' keys/values ``[T, Hkv, D]`` (fp32 or bf16) into the
     paged caches in place, stored as ``x / scale`` rounded to the cache dtype.
     ``max_qo_len`` defaults to the shape-only bound ``T - (B - 1)``;
-    ``num_cus`` 0 sizes the launch for the current device."""
+    ``num_cus`` 0 sizes the launch for the current device; ``k_cos_sin``
+    ([T, D] float32 cos/sin rows of the drafts' positions) rotates the keys by
+    RoPE first."""
     lib = load()
-    problem, args = _append_args(k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices,
-                                 last_page_len, qo_indptr, k_scale, v_scale, max_qo_len, stream,
-                                 num_cus)
-    _check(lib.vat_append_kv(*args), "vat_append_kv")
+    problem, args, rope = _append_args(k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices,
+                                       last_page_len, qo_indptr, k_scale, v_scale, max_qo_len,
+                                       stream, num_cus, k_cos_sin)
+    fn = lib.vat_append_kv_rope if rope else lib.vat_append_kv
+    _check(fn(*args), "vat_append_kv")
     return k_cache, v_cache
 
 
@@ -303,12 +325,14 @@ class PreparedAppend:
         self.lib = load()
         self.keep = (k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
                      qo_indptr)
-        self.problem, self.args = _append_args(k_new, v_new, k_cache, v_cache, kv_indptr,
-                                               kv_indices, last_page_len, qo_indptr, k_scale,
-                                               v_scale, max_qo_len, stream, num_cus)
+        self.problem, self.args, rope = _append_args(k_new, v_new, k_cache, v_cache, kv_indptr,
+                                                     kv_indices, last_page_len, qo_indptr,
+                                                     k_scale, v_scale, max_qo_len, stream,
+                                                     num_cus)
+        self.fn = self.lib.vat_append_kv_rope if rope else self.lib.vat_append_kv
 
     def __call__(self):
-        _check(self.lib.vat_append_kv(*self.args), "vat_append_kv")
+        _check(self.fn(*self.args), "vat_append_kv")
 
 
 class PreparedCall:

@@ -12,9 +12,10 @@
 namespace vat {
 const void* tile_kernel(int kv_dtype, int head_dim, int rt);
 const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int pair,
-                          int mask_mode);
+                          int mask_mode, int rope);
 const void* merge_kernel(int q_is_f32, int head_dim);
 const void* append_kernel(int src_dtype, int cache_dtype, int pow2_scales, int units);
+const void* append_rope_kernel(int src_dtype, int cache_dtype, int pow2_scales);
 }  // namespace vat
 
 namespace {
@@ -70,9 +71,9 @@ int page_shift(int32_t page_size) {
 vat_status_t prepare(const vat_problem_t* p, const void* q, const void* k_cache,
                      const void* v_cache, const int32_t* kv_indptr, const int32_t* kv_indices,
                      const int32_t* last_page_len, const int32_t* qo_indptr, const uint8_t* mask,
-                     const int32_t* mask_indptr, float sm_scale, float k_scale, float v_scale,
-                     void* out, float* lse, void* workspace, size_t workspace_bytes,
-                     vat_plan_t* plan) {
+                     const int32_t* mask_indptr, const float* q_cos_sin, float sm_scale,
+                     float k_scale, float v_scale, void* out, float* lse, void* workspace,
+                     size_t workspace_bytes, vat_plan_t* plan) {
   vat_status_t st = plan_for(p, plan);
   if (st != VAT_OK) return st;
   if (!(sm_scale > 0.f) || !isfinite(sm_scale) || !(k_scale > 0.f) || !isfinite(k_scale) ||
@@ -83,6 +84,8 @@ vat_status_t prepare(const vat_problem_t* p, const void* q, const void* k_cache,
       !out || !lse)
     return VAT_ERR_NULL;
   if (p->has_mask && (!mask || !mask_indptr)) return VAT_ERR_NULL;
+  if (p->rope && !q_cos_sin) return VAT_ERR_NULL;
+  if (p->rope && !aligned(q_cos_sin, 16)) return VAT_ERR_ALIGN;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
       !aligned(lse, 4) || !aligned(kv_indptr, 4) || !aligned(kv_indices, 4) ||
       !aligned(last_page_len, 4) || !aligned(qo_indptr, 4) ||
@@ -100,10 +103,11 @@ vat_status_t launch_partial(const vat_problem_t* p, const vat_plan_t& plan, cons
                             const void* k_cache, const void* v_cache, const int32_t* kv_indptr,
                             const int32_t* kv_indices, const int32_t* last_page_len,
                             const int32_t* qo_indptr, const uint8_t* mask,
-                            const int32_t* mask_indptr, float sm_scale, float k_scale,
-                            float v_scale, void* out, float* lse, void* workspace,
-                            hipStream_t stream) {
+                            const int32_t* mask_indptr, const float* q_cos_sin,
+                            float sm_scale, float k_scale, float v_scale, void* out, float* lse,
+                            void* workspace, hipStream_t stream) {
   vat::PartialArgs a;
+  a.q_cos_sin = p->rope ? q_cos_sin : nullptr;
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
@@ -140,7 +144,8 @@ vat_status_t launch_partial(const vat_problem_t* p, const vat_plan_t& plan, cons
   a.slices = plan.slices;
   a.block_order = plan.block_order;
   const void* fn = plan.kernel ? vat::stream_kernel(p->kv_dtype, p->head_dim, plan.row_tiles_per_wave,
-                                                    plan.dma_waves, plan.waves_keys, p->has_mask)
+                                                    plan.dma_waves, plan.waves_keys, p->has_mask,
+                                                    p->rope)
                                : vat::tile_kernel(p->kv_dtype, p->head_dim, plan.row_tiles_per_wave);
   if (plan.lds_bytes > 65536) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, plan.lds_bytes) !=
@@ -188,6 +193,74 @@ vat_status_t launch_merge(const vat_problem_t* p, const vat_plan_t& plan,
   return e == hipSuccess ? VAT_OK : VAT_ERR_HIP;
 }
 
+// The cache write; `rope` asks for keys rotated by the per-token cos/sin
+// rows `k_cos_sin` first.
+vat_status_t append_kv(const vat_problem_t* problem, int32_t src_dtype, const void* k_new,
+                       const void* v_new, void* k_cache, void* v_cache, const int32_t* kv_indptr,
+                       const int32_t* kv_indices, const int32_t* last_page_len,
+                       const int32_t* qo_indptr, const float* k_cos_sin, bool rope,
+                       float k_scale, float v_scale, hipStream_t stream) {
+  vat_status_t st = vat::validate_append(problem, src_dtype);
+  if (st != VAT_OK) return st;
+  if (!(k_scale > 0.f) || !isfinite(k_scale) || !(v_scale > 0.f) || !isfinite(v_scale))
+    return VAT_ERR_SHAPE;
+  const vat_problem_t& p = *problem;
+  if (p.batch == 0 || p.num_qo_tokens == 0 || p.max_qo_len == 0) return VAT_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !kv_indptr || !kv_indices || !last_page_len ||
+      !qo_indptr || (rope && !k_cos_sin))
+    return VAT_ERR_NULL;
+  if (rope && !aligned(k_cos_sin, 16)) return VAT_ERR_ALIGN;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(kv_indptr, 4) || !aligned(kv_indices, 4) ||
+      !aligned(last_page_len, 4) || !aligned(qo_indptr, 4))
+    return VAT_ERR_ALIGN;
+  vat::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.last_page_len = last_page_len;
+  a.qo_indptr = qo_indptr;
+  a.k_cos_sin = rope ? k_cos_sin : nullptr;
+  a.head_dim = p.head_dim;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  // A normal power of two has an exact reciprocal (2^-126 .. 2^126, the
+  // smallest as a subnormal), so x * (1 / s) rounds x / s exactly.
+  const bool pow2 = pow2_normal(k_scale) && pow2_normal(v_scale);
+  a.k_inv = pow2 ? 1.0f / k_scale : 0.f;
+  a.v_inv = pow2 ? 1.0f / v_scale : 0.f;
+  a.batch = p.batch;
+  a.row_units = p.num_kv_heads * p.head_dim / 8;
+  a.page_shift = page_shift(p.page_size);
+  a.num_pages = p.num_pages;
+  a.num_kv_indices = p.num_kv_indices;
+  a.tokens = p.num_qo_tokens;
+  // Two 8-element units per thread when the write covers every CU's 2048
+  // threads at least four times over (measured: 3 % to 12 % faster there);
+  // one otherwise, which halves the per-thread latency chain of small writes.
+  int32_t cus = p.num_cus;
+  if (cus == 0) {
+    st = device_cus(&cus);
+    if (st != VAT_OK) return st;
+  }
+  const int64_t total_units = 2 * int64_t(p.num_qo_tokens) * a.row_units;
+  const int units_per_thread = total_units >= int64_t(4) * cus * 2048 ? 2 : 1;
+  // Grid y covers max_qo_len tokens of K and V per request; the kernel loops
+  // over any remainder, so the bound only sizes the launch.
+  const int64_t units = 2 * int64_t(p.max_qo_len) * a.row_units;
+  const int64_t per_block = int64_t(vat::kAppendThreads) * (rope ? 1 : units_per_thread);
+  const int64_t gy = (units + per_block - 1) / per_block;
+  const void* fn = rope ? vat::append_rope_kernel(src_dtype, p.kv_dtype, pow2 ? 1 : 0)
+                        : vat::append_kernel(src_dtype, p.kv_dtype, pow2 ? 1 : 0, units_per_thread);
+  void* args[] = {&a};
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.batch, (unsigned)(gy < 65535 ? gy : 65535), 1),
+                                 dim3(vat::kAppendThreads, 1, 1), args, 0, stream);
+  return e == hipSuccess ? VAT_OK : VAT_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -215,12 +288,12 @@ vat_status_t vat_launch_partial(const vat_problem_t* problem, const void* q, con
                                 size_t workspace_bytes, void* stream) {
   vat_plan_t plan;
   vat_status_t st = prepare(problem, q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
-                            qo_indptr, mask, mask_indptr, sm_scale, k_scale, v_scale, out, lse,
-                            workspace, workspace_bytes, &plan);
+                            qo_indptr, mask, mask_indptr, nullptr, sm_scale, k_scale, v_scale,
+                            out, lse, workspace, workspace_bytes, &plan);
   if (st != VAT_OK || plan_is_empty(plan)) return st;
   return launch_partial(problem, plan, q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
-                        qo_indptr, mask, mask_indptr, sm_scale, k_scale, v_scale, out, lse,
-                        workspace, (hipStream_t)stream);
+                        qo_indptr, mask, mask_indptr, nullptr, sm_scale, k_scale, v_scale, out,
+                        lse, workspace, (hipStream_t)stream);
 }
 
 vat_status_t vat_launch_merge(const vat_problem_t* problem, const int32_t* kv_indptr,
@@ -246,14 +319,27 @@ vat_status_t verify_attention(const vat_problem_t* problem, const void* q, const
                               const int32_t* mask_indptr, float sm_scale, float k_scale,
                               float v_scale, void* out, float* lse, void* workspace,
                               size_t workspace_bytes, void* stream) {
+  return verify_attention_rope(problem, q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
+                               qo_indptr, mask, mask_indptr, nullptr, sm_scale, k_scale, v_scale,
+                               out, lse, workspace, workspace_bytes, stream);
+}
+
+vat_status_t verify_attention_rope(const vat_problem_t* problem, const void* q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* kv_indptr, const int32_t* kv_indices,
+                                   const int32_t* last_page_len, const int32_t* qo_indptr,
+                                   const uint8_t* mask, const int32_t* mask_indptr,
+                                   const float* q_cos_sin, float sm_scale, float k_scale,
+                                   float v_scale, void* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
   vat_plan_t plan;
   vat_status_t st = prepare(problem, q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
-                            qo_indptr, mask, mask_indptr, sm_scale, k_scale, v_scale, out, lse,
-                            workspace, workspace_bytes, &plan);
+                            qo_indptr, mask, mask_indptr, q_cos_sin, sm_scale, k_scale, v_scale,
+                            out, lse, workspace, workspace_bytes, &plan);
   if (st != VAT_OK || plan_is_empty(plan)) return st;
   st = launch_partial(problem, plan, q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
-                      qo_indptr, mask, mask_indptr, sm_scale, k_scale, v_scale, out, lse,
-                      workspace, (hipStream_t)stream);
+                      qo_indptr, mask, mask_indptr, q_cos_sin, sm_scale, k_scale, v_scale, out,
+                      lse, workspace, (hipStream_t)stream);
   if (st != VAT_OK) return st;
   return launch_merge(problem, plan, kv_indptr, last_page_len, qo_indptr, v_scale, out, lse,
                       workspace, (hipStream_t)stream);
@@ -264,61 +350,20 @@ vat_status_t vat_append_kv(const vat_problem_t* problem, int32_t src_dtype, cons
                            const int32_t* kv_indptr, const int32_t* kv_indices,
                            const int32_t* last_page_len, const int32_t* qo_indptr, float k_scale,
                            float v_scale, void* stream) {
-  vat_status_t st = vat::validate_append(problem, src_dtype);
-  if (st != VAT_OK) return st;
-  if (!(k_scale > 0.f) || !isfinite(k_scale) || !(v_scale > 0.f) || !isfinite(v_scale))
-    return VAT_ERR_SHAPE;
-  const vat_problem_t& p = *problem;
-  if (p.batch == 0 || p.num_qo_tokens == 0 || p.max_qo_len == 0) return VAT_OK;
-  if (!k_new || !v_new || !k_cache || !v_cache || !kv_indptr || !kv_indices || !last_page_len ||
-      !qo_indptr)
-    return VAT_ERR_NULL;
-  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
-      !aligned(v_cache, 16) || !aligned(kv_indptr, 4) || !aligned(kv_indices, 4) ||
-      !aligned(last_page_len, 4) || !aligned(qo_indptr, 4))
-    return VAT_ERR_ALIGN;
-  vat::AppendArgs a;
-  a.k_new = k_new;
-  a.v_new = v_new;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.kv_indptr = kv_indptr;
-  a.kv_indices = kv_indices;
-  a.last_page_len = last_page_len;
-  a.qo_indptr = qo_indptr;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
-  // A normal power of two has an exact reciprocal (2^-126 .. 2^126, the
-  // smallest as a subnormal), so x * (1 / s) rounds x / s exactly.
-  const bool pow2 = pow2_normal(k_scale) && pow2_normal(v_scale);
-  a.k_inv = pow2 ? 1.0f / k_scale : 0.f;
-  a.v_inv = pow2 ? 1.0f / v_scale : 0.f;
-  a.batch = p.batch;
-  a.row_units = p.num_kv_heads * p.head_dim / 8;
-  a.page_shift = page_shift(p.page_size);
-  a.num_pages = p.num_pages;
-  a.num_kv_indices = p.num_kv_indices;
-  a.tokens = p.num_qo_tokens;
-  // Two 8-element units per thread when the write covers every CU's 2048
-  // threads at least four times over (measured: 3 % to 12 % faster there);
-  // one otherwise, which halves the per-thread latency chain of small writes.
-  int32_t cus = p.num_cus;
-  if (cus == 0) {
-    st = device_cus(&cus);
-    if (st != VAT_OK) return st;
-  }
-  const int64_t total_units = 2 * int64_t(p.num_qo_tokens) * a.row_units;
-  const int units_per_thread = total_units >= int64_t(4) * cus * 2048 ? 2 : 1;
-  // Grid y covers max_qo_len tokens of K and V per request; the kernel loops
-  // over any remainder, so the bound only sizes the launch.
-  const int64_t units = 2 * int64_t(p.max_qo_len) * a.row_units;
-  const int64_t per_block = int64_t(vat::kAppendThreads) * units_per_thread;
-  const int64_t gy = (units + per_block - 1) / per_block;
-  const void* fn = vat::append_kernel(src_dtype, p.kv_dtype, pow2 ? 1 : 0, units_per_thread);
-  void* args[] = {&a};
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.batch, (unsigned)(gy < 65535 ? gy : 65535), 1),
-                                 dim3(vat::kAppendThreads, 1, 1), args, 0, (hipStream_t)stream);
-  return e == hipSuccess ? VAT_OK : VAT_ERR_HIP;
+  return append_kv(problem, src_dtype, k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices,
+                   last_page_len, qo_indptr, nullptr, false, k_scale, v_scale,
+                   (hipStream_t)stream);
+}
+
+vat_status_t vat_append_kv_rope(const vat_problem_t* problem, int32_t src_dtype,
+                                const void* k_new, const void* v_new, void* k_cache,
+                                void* v_cache, const int32_t* kv_indptr,
+                                const int32_t* kv_indices, const int32_t* last_page_len,
+                                const int32_t* qo_indptr, const float* k_cos_sin, float k_scale,
+                                float v_scale, void* stream) {
+  return append_kv(problem, src_dtype, k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices,
+                   last_page_len, qo_indptr, k_cos_sin, true, k_scale, v_scale,
+                   (hipStream_t)stream);
 }
 
 const char* vat_status_string(vat_status_t status) {

@@ -194,6 +194,87 @@ __global__ __launch_bounds__(kAppendThreads) void vat_append(AppendArgs a) {
   }
 }
 
+// Eight rotated key elements, fed to Store8 like a source chunk.
+struct F8 {
+  float v[8];
+  __device__ __forceinline__ float get(int i) const { return v[i]; }
+};
+
+// The write with the keys rotated by RoPE first (LLaMA style: dimension i
+// pairs with i + D/2, i < D/2, by the token's cos/sin row: x'_i = x_i c_i -
+// x_{i+D/2} s_i, x'_{i+D/2} = x_{i+D/2} c_i + x_i s_i), in binary32 with every
+// product and sum rounded on its own, then scaled and rounded as above. Key
+// unit (t, h, j) moves elements [8 j, 8 j + 8) of head h and their partners
+// D/2 further; value units are the plain ones. One unit per thread.
+template <int SRC, int DST, bool POW2>
+__global__ __launch_bounds__(kAppendThreads) void vat_append_rope(AppendArgs a) {
+  const int b = blockIdx.x;
+  const Req r = make_req(a.kv_indptr[b], a.kv_indptr[b + 1], a.last_page_len[b], a.qo_indptr[b],
+                         a.qo_indptr[b + 1], 0, a.page_shift, a.num_kv_indices, a.tokens);
+  const int D = a.head_dim;
+  const unsigned ru = (unsigned)a.row_units;  // 8-element units per token row
+  const unsigned rk = ru / 2;                 // key units (element pairs of 8) per row
+  const unsigned jd = (unsigned)(D / 16);     // key units per head
+  const unsigned per_k = (unsigned)r.L * rk;
+  const unsigned units = per_k + (unsigned)r.L * ru;
+  const long long row_elems = (long long)ru * 8;
+  const int slot_mask = (1 << a.page_shift) - 1;
+  for (unsigned u = blockIdx.y * kAppendThreads + threadIdx.x; u < units;
+       u += gridDim.y * kAppendThreads) {
+    if (u < per_k) {
+      const unsigned t = u / rk;
+      const unsigned w = u - t * rk;
+      const unsigned h = w / jd, j = w - h * jd;
+      const int lo = (int)(h * D + 8 * j), hi = lo + D / 2;
+      const int n = r.prefix + (int)t;
+      const int page = a.kv_indices[r.kv_start + (n >> a.page_shift)];
+      const long long row = (long long)(r.q_start + (int)t);
+      Src8<SRC> xl, xh;
+      xl.load(a.k_new, row * row_elems + lo);
+      xh.load(a.k_new, row * row_elems + hi);
+      const f32x4* cs = reinterpret_cast<const f32x4*>(a.k_cos_sin + row * D + 8 * j);
+      const f32x4 c0 = cs[0], c1 = cs[1];
+      const f32x4 s0 = cs[D / 8], s1 = cs[D / 8 + 1];
+      if (page < 0 || page >= a.num_pages) continue;
+      const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+      const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+      F8 yl, yh;
+      {
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pl = xl.get(e) * c[e], ph = xh.get(e) * sn[e];
+          const float ql = xh.get(e) * c[e], qh = xl.get(e) * sn[e];
+          yl.v[e] = pl - ph;
+          yh.v[e] = ql + qh;
+        }
+      }
+      // A NaN from the rotation (a NaN input, or infinity times zero) takes
+      // the canonical positive NaN: its sign would otherwise depend on how
+      // the hardware forms invalid results.
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        yl.v[e] = yl.v[e] != yl.v[e] ? __builtin_bit_cast(float, 0x7fc00000u) : yl.v[e];
+        yh.v[e] = yh.v[e] != yh.v[e] ? __builtin_bit_cast(float, 0x7fc00000u) : yh.v[e];
+      }
+      const long long slot_row = ((long long)page << a.page_shift) + (n & slot_mask);
+      Store8<DST>::template run<POW2>(a.k_cache, slot_row * row_elems + lo, yl, a.k_scale, a.k_inv);
+      Store8<DST>::template run<POW2>(a.k_cache, slot_row * row_elems + hi, yh, a.k_scale, a.k_inv);
+    } else {
+      const unsigned uu = u - per_k;
+      const unsigned t = uu / ru;
+      const int w = (int)(uu - t * ru);
+      const int n = r.prefix + (int)t;
+      const int page = a.kv_indices[r.kv_start + (n >> a.page_shift)];
+      Src8<SRC> x;
+      x.load(a.v_new, (long long)(r.q_start + (int)t) * row_elems + w * 8);
+      if (page < 0 || page >= a.num_pages) continue;
+      const long long slot_row = ((long long)page << a.page_shift) + (n & slot_mask);
+      Store8<DST>::template run<POW2>(a.v_cache, slot_row * row_elems + w * 8, x, a.v_scale, a.v_inv);
+    }
+  }
+}
+
 }  // namespace
 
 template <int SRC, int DST>
@@ -201,6 +282,25 @@ const void* pick(bool pow2, int units) {
   if (units == 2)
     return pow2 ? (const void*)vat_append<SRC, DST, true, 2> : (const void*)vat_append<SRC, DST, false, 2>;
   return pow2 ? (const void*)vat_append<SRC, DST, true, 1> : (const void*)vat_append<SRC, DST, false, 1>;
+}
+
+template <int SRC, int DST>
+const void* pick_rope(bool pow2) {
+  return pow2 ? (const void*)vat_append_rope<SRC, DST, true> : (const void*)vat_append_rope<SRC, DST, false>;
+}
+
+const void* append_rope_kernel(int src_dtype, int cache_dtype, int pow2_scales) {
+  const bool p = pow2_scales != 0;
+  if (src_dtype == KV_BF16) {
+    if (cache_dtype == KV_BF16) return pick_rope<KV_BF16, KV_BF16>(p);
+    if (cache_dtype == KV_E4M3) return pick_rope<KV_BF16, KV_E4M3>(p);
+    if (cache_dtype == KV_F32) return pick_rope<KV_BF16, KV_F32>(p);
+  } else if (src_dtype == KV_F32) {
+    if (cache_dtype == KV_BF16) return pick_rope<KV_F32, KV_BF16>(p);
+    if (cache_dtype == KV_E4M3) return pick_rope<KV_F32, KV_E4M3>(p);
+    if (cache_dtype == KV_F32) return pick_rope<KV_F32, KV_F32>(p);
+  }
+  return nullptr;
 }
 
 const void* append_kernel(int src_dtype, int cache_dtype, int pow2_scales, int units) {

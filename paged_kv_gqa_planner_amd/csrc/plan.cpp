@@ -37,6 +37,11 @@ vat_status_t validate_problem(const vat_problem_t* p) {
   if (p->has_mask < 0 || p->has_mask > 2) return VAT_ERR_SHAPE;
   if (p->has_mask && p->max_qo_len > kMaxMaskedLen) return VAT_ERR_UNSUPPORTED;
   if (p->has_mask && p->num_mask_bytes < 1) return VAT_ERR_SHAPE;
+  if (p->rope != 0 && p->rope != 1) return VAT_ERR_SHAPE;
+  // Query RoPE runs in the streaming kernel, without byte-row masks.
+  if (p->rope && (p->kv_dtype == VAT_F32 ||
+                  (p->kv_dtype == VAT_FP8_E4M3FN && p->head_dim == 64) || p->has_mask == 2))
+    return VAT_ERR_UNSUPPORTED;
   if (p->chunk_keys < -1 || (p->chunk_keys > 0 && p->chunk_keys % kChunkQuantum))
     return VAT_ERR_SHAPE;
   if (p->batch > 0 && p->num_qo_tokens > 0 && p->num_pages < 1) return VAT_ERR_SHAPE;
@@ -106,8 +111,10 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   const bool stream = (p->kv_dtype != VAT_F32) && !(fp8 && p->head_dim == 64);
   int dw = 0;
   if (stream) {
-    // fp8 and full byte-row masks keep one row tile per wave (registers).
-    const int64_t max_tiles = (fp8 || p->has_mask == 2) ? kStreamThreads / 64 : kStreamMaxTiles;
+    // fp8, full byte-row masks and query RoPE keep one row tile per wave
+    // (registers).
+    const int64_t max_tiles =
+        (fp8 || p->has_mask == 2 || p->rope) ? kStreamThreads / 64 : kStreamMaxTiles;
     const int64_t bt = tiles <= max_tiles ? tiles : max_tiles;  // tiles per row block
     rt = bt <= kStreamThreads / 64 ? 1 : 2;
     wr = int(cdiv(bt, rt));

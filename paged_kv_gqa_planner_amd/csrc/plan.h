@@ -65,6 +65,7 @@ struct PartialArgs {
   int32_t chunk_keys, num_ids, has_mask;
   int32_t slices;  // > 0: balanced page slices per KV head (streaming kernel, B <= 64)
   int32_t block_order;  // 1: one-dimensional grid, row blocks of a group on one XCD
+  const float* q_cos_sin;  // [T, D] RoPE cos/sin row per query token, or null
 };
 
 // Arguments of the merge kernel.
@@ -93,8 +94,10 @@ struct AppendArgs {
   const int32_t* kv_indices;
   const int32_t* last_page_len;
   const int32_t* qo_indptr;
+  const float* k_cos_sin;  // [T, D] RoPE cos/sin row per draft token, or null
   float k_scale, v_scale;
   float k_inv, v_inv;  // exact 1 / scale when both scales are powers of two
+  int32_t head_dim;
   int32_t batch;
   int32_t row_units;  // Hkv * D / 8: 8-element units in one token row
   int32_t page_shift;

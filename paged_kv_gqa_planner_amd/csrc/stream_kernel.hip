@@ -179,8 +179,11 @@ __device__ __forceinline__ void keep_branch() { asm volatile(""); }
 // while tile kt's PV MFMAs run.
 // KT: 16-key tiles this wave takes, tiles kt0 .. kt0 + KT - 1 of an SK-key
 // stage.
-template <int KV, int D, int RT, int KT, int SK = kStageKeys>
+// QLO: the queries are carried as two bf16 terms (qf + qlo, a rotated query
+// that bf16 alone would round), and S^T takes one MFMA per term.
+template <int KV, int D, int RT, int KT, int SK = kStageKeys, bool QLO = false>
 __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsigned (&qf)[RT][D / 8],
+                                              const unsigned (&qlo)[RT][QLO ? D / 8 : 1],
                                               const int (&row_t)[RT],
                                               const unsigned long long (&row_bits)[RT],
                                               const Vis& vis, const unsigned char* stage, int n0,
@@ -222,6 +225,11 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
         const u32x4 qw = {qf[rt][4 * ks], qf[rt][4 * ks + 1], qf[rt][4 * ks + 2], qf[rt][4 * ks + 3]};
         st[kt][rt] =
             __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kt], __builtin_bit_cast(bf16x8, qw), st[kt][rt], 0, 0, 0);
+        if constexpr (QLO) {
+          const u32x4 ql = {qlo[rt][4 * ks], qlo[rt][4 * ks + 1], qlo[rt][4 * ks + 2], qlo[rt][4 * ks + 3]};
+          st[kt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kt], __builtin_bit_cast(bf16x8, ql),
+                                                               st[kt][rt], 0, 0, 0);
+        }
       }
   }
   // ---- keys past the item, drafts under causal / mask. Lane (row, j) holds
@@ -418,14 +426,19 @@ __device__ __forceinline__ void fill_window(int* win, const PartialArgs& a, int 
 // take at most nine bytes from the row's first, three per lane; full byte
 // rows (mode 2, ROWS) one byte per draft, sixteen per lane -- registers that
 // only the ROWS instantiations (one row tile per wave) carry.
-template <int KV, int D, int RT, bool ROWS>
+template <int KV, int D, int RT, bool ROWS, bool ROPE = false>
 struct RowSet {
   static constexpr int kRaw = ROWS ? 16 : 3;
+  // RoPE: cos then sin of the lane's rotated dimension pairs, 16 per 32-wide
+  // d step of the first half (ROPE instantiations only).
+  static constexpr int kCs = ROPE ? (D / 32 / 2) * 16 : 1;
   int row_t[RT], row_g[RT];
   bool row_ok[RT];
   unsigned long long row_bits[RT];
   unsigned qf[RT][D / 8];
   unsigned raw[RT][kRaw];  // this lane's share of the row's mask bytes
+  unsigned csr[RT][kCs];   // RoPE cos/sin of the row's token (ROPE)
+  unsigned qlo[RT][ROPE ? D / 8 : 1];  // ROPE: bf16 remainder of the rotated query
 
   __device__ __forceinline__ void fetch(const PartialArgs& a, int q_start, int L, int prefix,
                                         int mask_off, int row0, int h, int lane) {
@@ -452,6 +465,28 @@ struct RowSet {
         qf[rt][4 * ks + 3] = x.w;
       }
       const int t = min(row_t[rt], L - 1);
+      if constexpr (ROPE) {
+        // The 32-wide d steps ks < D / 64 hold the first halves of the rotated
+        // pairs, and step ks + D / 64 of the same lane their partners: the
+        // lane needs cos/sin of its 8 dimensions at each of the former.
+        const float* cs = a.q_cos_sin + (long long)(q_start + t) * D;
+#pragma unroll
+        for (int ks = 0; ks < D / 64; ++ks) {
+          const int d0 = (KV == KV_E4M3) ? 64 * (ks >> 1) + 16 * j4 + 8 * (ks & 1) : 32 * ks + 8 * j4;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+              const u32x4 w = *(const u32x4*)(cs + half * (D / 2) + d0 + 4 * k);
+              unsigned* dst = &csr[rt][ks * 16 + half * 8 + 4 * k];
+              dst[0] = w.x;
+              dst[1] = w.y;
+              dst[2] = w.z;
+              dst[3] = w.w;
+            }
+          }
+        }
+      }
       if constexpr (ROWS) {
         // Draft j of row t: byte mask_off + t (prefix + L) + prefix + j.
         const long long byte0 = mask_off + (long long)t * (prefix + L) + prefix + 16 * j4;
@@ -471,9 +506,41 @@ struct RowSet {
     const int j4 = lane >> 4;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
+      if constexpr (ROPE) {
+        // x' = x c - y s, y' = y c + x s for the pair (x at step ks, y at step
+        // ks + D / 64, same element), rounded back to bf16.
+#pragma unroll
+        for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            unsigned& wx = qf[rt][4 * ks + e / 2];
+            unsigned& wy = qf[rt][4 * (ks + D / 64) + e / 2];
+            const int sh = 16 * (e & 1);
+            const float x = __builtin_bit_cast(float, ((wx >> sh) & 0xffffu) << 16);
+            const float y = __builtin_bit_cast(float, ((wy >> sh) & 0xffffu) << 16);
+            const float c = __builtin_bit_cast(float, csr[rt][ks * 16 + e]);
+            const float sn = __builtin_bit_cast(float, csr[rt][ks * 16 + 8 + e]);
+            const float rx = x * c - y * sn, ry = y * c + x * sn;
+            const unsigned nx = f32_to_bf16_bits(rx), ny = f32_to_bf16_bits(ry);
+            // The rotated value split into two bf16 terms: rx ~ hi + lo to
+            // about 2^-17 relative (hi alone would be 2^-9).
+            const unsigned lx = f32_to_bf16_bits(rx - __builtin_bit_cast(float, nx << 16));
+            const unsigned ly = f32_to_bf16_bits(ry - __builtin_bit_cast(float, ny << 16));
+            wx = (wx & ~(0xffffu << sh)) | (nx << sh);
+            wy = (wy & ~(0xffffu << sh)) | (ny << sh);
+            unsigned& lwx = qlo[rt][4 * ks + e / 2];
+            unsigned& lwy = qlo[rt][4 * (ks + D / 64) + e / 2];
+            lwx = (lwx & ~(0xffffu << sh)) | (lx << sh);
+            lwy = (lwy & ~(0xffffu << sh)) | (ly << sh);
+          }
+      }
       if (!row_ok[rt]) {
 #pragma unroll
         for (int k = 0; k < D / 8; ++k) qf[rt][k] = 0u;
+        if constexpr (ROPE) {
+#pragma unroll
+          for (int k = 0; k < D / 8; ++k) qlo[rt][k] = 0u;
+        }
       }
       // This lane's bits of the row, then the OR over its four lanes.
       unsigned long long part = 0;
@@ -510,9 +577,9 @@ struct RowSet {
 // fp32 partial (v_scale not yet applied) and its base-2 log-sum-exp in slot
 // `slot`.
 // `rb`: row block; `row0`: this wave's first row within the block.
-template <int KV, int D, int RT, bool ROWS>
+template <int KV, int D, int RT, bool ROWS, bool ROPE>
 __device__ __forceinline__ void write_rows(const StreamAcc<D, RT>& acc, const float (&lrow)[RT],
-                                           const RowSet<KV, D, RT, ROWS>& rs, const PartialArgs& a,
+                                           const RowSet<KV, D, RT, ROWS, ROPE>& rs, const PartialArgs& a,
                                            int q_start, bool whole, int slot, int rb, int row0,
                                            int h, int lane) {
   constexpr int NDT = D / 16;
@@ -605,7 +672,7 @@ __device__ __forceinline__ void merge_pair_state(StreamAcc<D, RT>& acc, float (&
 // through one ring of LDS buffers filled by DMA. Wave w < waves_rows owns row
 // tiles [w RT, w RT + RT) of every segment and runs all of its keys, so no
 // two waves ever hold parts of the same row; all eight waves issue the DMA.
-template <int KV, int D, int RT, int NS, int DW, int P, int SK, bool ROWS>
+template <int KV, int D, int RT, int NS, int DW, int P, int SK, bool ROWS, bool ROPE>
 __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   using G = StreamGeom<KV, D, DW, SK>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -729,7 +796,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   const int row0 = tset * RT * 16;                  // within the row block
   const int rbase = rb * a.rows_per_block + row0;   // in the request's rows
   float* pair_slot = (float*)(smem + NS * G::STAGE + kStreamPageWindow * 4) + tset * PairSlot<D, RT>::FLOATS;
-  RowSet<KV, D, RT, ROWS> rs;
+  RowSet<KV, D, RT, ROWS, ROPE> rs;
   StreamAcc<D, RT> acc;
   Vis vis{0, 0, a.has_mask, 0};
   bool has_rows = false;
@@ -816,7 +883,8 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
     if (computes && has_rows) {
       const int n0 = lane_val(sg.lo, s) + (g - first) * SK;
       const unsigned char* stage = smem + (g % NS) * G::STAGE;
-      compute_stage<KV, D, RT, SK / 16 / P, SK>(acc, rs.qf, rs.row_t, rs.row_bits, vis, stage, n0,
+      compute_stage<KV, D, RT, SK / 16 / P, SK, ROPE>(acc, rs.qf, rs.qlo, rs.row_t, rs.row_bits, vis,
+                                                      stage, n0,
                                                 a.c_log2, lane, phase * (SK / 16 / P));
     }
     if (g == lane_val(sg.incl, s) - 1) {
@@ -831,7 +899,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
         for (int rt = 0; rt < RT; ++rt) lrow[rt] = rowsum4_v(acc.l[rt]);
       }
       if (computes && has_rows && phase == 0)
-        write_rows<KV, D, RT, ROWS>(acc, lrow, rs, a, lane_val(sg.q_start, s), lane_val(sg.whole, s) != 0,
+        write_rows<KV, D, RT, ROWS, ROPE>(acc, lrow, rs, a, lane_val(sg.q_start, s), lane_val(sg.whole, s) != 0,
                               lane_val(sg.slot, s), rb, row0, h, lane);
     }
   }
@@ -844,32 +912,39 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
 // 32 KB (64 bf16 keys of D = 128, else 128 keys); four of them fill the
 // 128 KB the planner gives the ring.
 template <int KV, int D, int NS, int SK>
-static const void* stream_variant(int rt, int dma_waves, int pair, bool rows) {
+static const void* stream_variant(int rt, int dma_waves, int pair, bool rows, bool rope) {
+  if (rope) {
+    // Queries rotated by RoPE at the row fetch: one row tile per wave.
+    if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK, false, true>;
+    if (dma_waves == 2) return (const void*)vat_stream<KV, D, 1, NS, 2, 1, SK, false, true>;
+    return pair == 2 ? (const void*)vat_stream<KV, D, 1, NS, 4, 2, SK, false, true>
+                     : (const void*)vat_stream<KV, D, 1, NS, 4, 1, SK, false, true>;
+  }
   if (rows) {
     // Full byte-row masks: one row tile per wave (the planner's choice).
-    if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK, true>;
-    if (dma_waves == 2) return (const void*)vat_stream<KV, D, 1, NS, 2, 1, SK, true>;
-    return pair == 2 ? (const void*)vat_stream<KV, D, 1, NS, 4, 2, SK, true>
-                     : (const void*)vat_stream<KV, D, 1, NS, 4, 1, SK, true>;
+    if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK, true, false>;
+    if (dma_waves == 2) return (const void*)vat_stream<KV, D, 1, NS, 2, 1, SK, true, false>;
+    return pair == 2 ? (const void*)vat_stream<KV, D, 1, NS, 4, 2, SK, true, false>
+                     : (const void*)vat_stream<KV, D, 1, NS, 4, 1, SK, true, false>;
   }
   if constexpr (KV != KV_E4M3)
-    if (rt == 2) return (const void*)vat_stream<KV, D, 2, NS, kSWaves, 1, SK, false>;
-  if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK, false>;
-  if (dma_waves == 2) return (const void*)vat_stream<KV, D, 1, NS, 2, 1, SK, false>;
-  return pair == 2 ? (const void*)vat_stream<KV, D, 1, NS, 4, 2, SK, false>
-                   : (const void*)vat_stream<KV, D, 1, NS, 4, 1, SK, false>;
+    if (rt == 2) return (const void*)vat_stream<KV, D, 2, NS, kSWaves, 1, SK, false, false>;
+  if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK, false, false>;
+  if (dma_waves == 2) return (const void*)vat_stream<KV, D, 1, NS, 2, 1, SK, false, false>;
+  return pair == 2 ? (const void*)vat_stream<KV, D, 1, NS, 4, 2, SK, false, false>
+                   : (const void*)vat_stream<KV, D, 1, NS, 4, 1, SK, false, false>;
 }
 
 const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int pair,
-                          int mask_mode) {
+                          int mask_mode, int rope) {
   static_assert(stream_stage_keys(KV_BF16, 128) == 64 && stream_stage_keys(KV_BF16, 64) == 128 &&
                 stream_stage_keys(KV_E4M3, 128) == 128, "stage sizes match the planner");
-  const bool rows = mask_mode == 2;
+  const bool rows = mask_mode == 2, ro = rope != 0;
   if (kv_dtype == KV_BF16)
-    return head_dim == 128 ? stream_variant<KV_BF16, 128, 4, 64>(rt, dma_waves, pair, rows)
-                           : stream_variant<KV_BF16, 64, 4, 128>(rt, dma_waves, pair, rows);
+    return head_dim == 128 ? stream_variant<KV_BF16, 128, 4, 64>(rt, dma_waves, pair, rows, ro)
+                           : stream_variant<KV_BF16, 64, 4, 128>(rt, dma_waves, pair, rows, ro);
   // The planner keeps fp8 at one row tile per wave.
-  return stream_variant<KV_E4M3, 128, 4, 128>(1, dma_waves, pair, rows);
+  return stream_variant<KV_E4M3, 128, 4, 128>(1, dma_waves, pair, rows, ro);
 }
 
 }  // namespace vat

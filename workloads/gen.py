@@ -499,14 +499,14 @@ def tree_depths(parents: Sequence[int]) -> np.ndarray:
 
 def rope_positions(p: Problem) -> np.ndarray:
     """Position of every query/draft token row: ``prefix_b`` plus its depth in
-    the request's tree (a chain, or no mask: its index t)."""
+    the request's tree (a chain, a random mask or no mask: its index t)."""
     pos = np.zeros(p.num_tokens, dtype=np.int64)
     parents = p.info.get("parents")
     for b in range(p.batch):
         r0, r1 = int(p.qo_indptr[b]), int(p.qo_indptr[b + 1])
         L = r1 - r0
         prefix = p.info["kv_lens"][b] - L
-        if parents is not None and parents[b] is not None and len(parents[b]) == L:
+        if parents is not None and b < len(parents) and len(parents[b]) == L:
             pos[r0:r1] = prefix + tree_depths(parents[b])
         else:
             pos[r0:r1] = prefix + np.arange(L)
