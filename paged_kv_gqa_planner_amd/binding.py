@@ -128,7 +128,7 @@ def make_problem(*, batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_
                  num_mask_bytes=0, num_cus=0, chunk_keys=-1, rope=0) -> VatProblem:
     return VatProblem(batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_pages,
                       num_kv_indices, num_qo_tokens, max_qo_len, q_dtype, kv_dtype,
-                      int(has_mask), num_mask_bytes, num_cus, chunk_keys, int(bool(rope)))
+                      int(has_mask), num_mask_bytes, num_cus, chunk_keys, int(rope))
 
 
 MASK_LAYOUTS = {"bits": 1, "rows": 2}

@@ -355,6 +355,32 @@ def test_append_host_checks_before_any_launch(lib):
                                      chunk_keys=-7), ptrs=dict(kn=0)) == 1
 
 
+def test_rope_host_checks(lib):
+    fake = 0x10000
+    prob = base_problem(chunk_keys=0, rope=1)
+
+    def call(cs, problem=prob):
+        return lib.verify_attention_rope(ctypes.byref(problem), fake, fake, fake, fake, fake, fake,
+                                         fake, 0, 0, cs, 0.1, 1.0, 1.0, fake, fake, 0, 0, None)
+
+    assert call(0) == 1                      # rope without cos/sin rows
+    assert call(fake + 4) == 4               # rows not 16-byte aligned
+    # The plain entry point passes no rows: a rope problem is refused there.
+    assert _call(lib, prob) == 1
+    for kw, code in [(dict(q_dtype=0, kv_dtype=0), 3), (dict(kv_dtype=2, head_dim=64), 3),
+                     (dict(has_mask=2, num_mask_bytes=100), 3), (dict(rope=2), 2)]:
+        bad = base_problem(chunk_keys=0, rope=kw.pop("rope", 1), **kw)
+        assert call(fake, bad) == code, kw
+    # Byte-row masks and fp32 caches plan normally without rope.
+    assert B.vat_plan(base_problem(has_mask=2, num_mask_bytes=100)).kernel == 1
+    plan = B.vat_plan(base_problem(rope=1, num_qo_heads=32, max_qo_len=64, num_qo_tokens=128))
+    assert plan.row_tiles_per_wave == 1 and plan.rows_per_block <= 128
+    ap = base_problem(kv_dtype=2)
+    args = [ctypes.byref(ap), 1] + [fake] * 8
+    assert lib.vat_append_kv_rope(*args, 0, 1.0, 1.0, None) == 1
+    assert lib.vat_append_kv_rope(*args, fake + 8, 1.0, 1.0, None) == 4
+
+
 def test_append_of_nothing_returns_ok_without_a_gpu(lib):
     assert _append(lib, base_problem(num_qo_tokens=0), ptrs=dict(kn=0, vn=0)) == 0
     assert _append(lib, base_problem(batch=0, num_qo_tokens=0)) == 0
