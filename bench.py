@@ -101,7 +101,7 @@ def algorithmic_work(p):
     return kvb, flops
 
 
-def timed_oracle(p, min_seconds: float, requests=None):
+def timed_oracle(p, min_seconds: float, requests=None, q_cos_sin=None):
     """Oracle wall time on this host with one BLAS thread; repeats the sample
     until ``min_seconds`` have passed (at least once)."""
     from threadpoolctl import threadpool_limits
@@ -115,7 +115,8 @@ def timed_oracle(p, min_seconds: float, requests=None):
             ref = oracle_va(p.q, p.k_cache, p.v_cache, p.kv_indptr, p.kv_indices, p.last_page_len,
                             p.qo_indptr, p.mask, p.mask_indptr, sm_scale=p.sm_scale,
                             k_scale=p.k_scale, v_scale=p.v_scale, q_dtype=p.q_dtype,
-                            kv_dtype=p.kv_dtype, requests=requests, mask_layout=p.mask_layout)
+                            kv_dtype=p.kv_dtype, requests=requests, mask_layout=p.mask_layout,
+                            q_cos_sin=q_cos_sin)
             reps += 1
             if time.perf_counter() - t0 >= min_seconds:
                 break
@@ -177,6 +178,11 @@ def bench_append(args, p, dev):
     spread = 2.0 if p.kv_dtype == "e4m3" else 1.0
     ks, vs = p.k_scale, p.v_scale
     T = p.num_tokens
+    k_rows = None
+    if args.rope:
+        from workloads import rope_cos_sin, rope_positions
+
+        k_rows = rope_cos_sin(rope_positions(p), p.head_dim)
     k_new, v_new = make_append_inputs(p, src, seed=1000 + args.config, spread=spread)
     base = to_device(p, dev)
     se = 4 if src == "f32" else 2
@@ -206,7 +212,9 @@ def bench_append(args, p, dev):
         calls.append(binding.PreparedAppend(kn, vn, base["k_cache"], base["v_cache"],
                                             base["kv_indptr"], idx, base["last_page_len"],
                                             base["qo_indptr"], k_scale=ks, v_scale=vs,
-                                            max_qo_len=p.max_qo_len))
+                                            max_qo_len=p.max_qo_len,
+                                            k_cos_sin=None if k_rows is None
+                                            else torch.from_numpy(k_rows).to(dev)))
     torch.cuda.synchronize()
 
     def raw(t):
@@ -228,7 +236,8 @@ def bench_append(args, p, dev):
         while True:
             want_k, want_v = oracle_append(k_new, v_new, src, p.k_cache, p.v_cache, p.kv_dtype,
                                            p.kv_indptr, p.kv_indices, p.last_page_len,
-                                           p.qo_indptr, p.page_size, k_scale=ks, v_scale=vs)
+                                           p.qo_indptr, p.page_size, k_scale=ks, v_scale=vs,
+                                           k_cos_sin=k_rows)
             reps += 1
             if args.no_cpu_baseline or time.perf_counter() - t_cpu >= args.cpu_seconds:
                 break
@@ -288,12 +297,14 @@ def bench_append(args, p, dev):
         "dtype": f"{src}->{p.kv_dtype}",
         "data": "synthetic",
         "config": {"workload": "draft K/V write of: " +
-                   WORKLOAD_NAMES[args.config].format(p=args.prefix),
+                   WORKLOAD_NAMES[args.config].format(p=args.prefix) +
+                   (", keys rotated by RoPE at their tree positions" if args.rope else ""),
                    "tokens": T, "kv_heads": p.num_kv_heads, "head_dim": p.head_dim,
                    "source_copies": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": profiled_traffic(f"append:{args.config}", append_source_hash()),
+                     "traffic": profiled_traffic(f"append:{args.config}" + (":rope" if args.rope else ""),
+                                                 append_source_hash()),
                      "kernel": "vat_append",
                      "algorithmic_bytes_per_launch": alg_bytes},
         "verified": verified,
@@ -319,6 +330,9 @@ def main():
                     help="verify: the attention path; append: the draft K/V cache write")
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--prefix", type=int, default=4096, help="prefix length for config 3")
+    ap.add_argument("--rope", action="store_true",
+                    help="rotate the queries by RoPE at their tree positions inside the kernel "
+                         "(verify) / the keys at the cache write (append)")
     ap.add_argument("--mask-layout", default="bits", choices=["bits", "rows"],
                     help="tree-mask layout for config 3: packed L x L bits or sglang's full "
                          "byte rows")
@@ -373,6 +387,12 @@ def main():
     pool_bytes = 2 * base["k_cache"].numel() * base["k_cache"].element_size()
     copies = args.copies or max(2, math.ceil((1 << 30) / pool_bytes))
 
+    q_cs = None
+    if args.rope:
+        from workloads import rope_cos_sin, rope_positions
+
+        rope_rows = rope_cos_sin(rope_positions(p), p.head_dim)
+        q_cs = torch.from_numpy(rope_rows).to(dev)
     # Physically permuted copies of the page pool, each with its own table.
     gen = torch.Generator(device="cpu").manual_seed(1234)
     batches = []
@@ -392,7 +412,7 @@ def main():
             base["q"], kc, vc, base["kv_indptr"], idx, base["last_page_len"], base["qo_indptr"],
             base["mask"], base["mask_indptr"], sm_scale=p.sm_scale, k_scale=p.k_scale,
             v_scale=p.v_scale, max_qo_len=p.max_qo_len, chunk_keys=args.chunk_keys,
-            mask_layout=p.mask_layout)
+            mask_layout=p.mask_layout, q_cos_sin=q_cs)
         batches.append(call)
     torch.cuda.synchronize()
 
@@ -400,11 +420,11 @@ def main():
     sample_requests = [0, p.batch - 1] if args.config in (4, 7) else None
     cpu = None
     if not args.no_cpu_baseline:
-        ref, cpu_s, cpu_reps = timed_oracle(p, args.cpu_seconds, sample_requests)
+        ref, cpu_s, cpu_reps = timed_oracle(p, args.cpu_seconds, sample_requests,
+                                            None if q_cs is None else rope_rows)
         cpu = (cpu_s, cpu_reps)
     else:
-        from tests.gpu_helpers import oracle_of
-        ref = oracle_of(p, requests=sample_requests)
+        ref, _, _ = timed_oracle(p, 0.0, sample_requests, None if q_cs is None else rope_rows)
     o0, l0 = batches[0]()
     torch.cuda.synchronize()
     o0 = o0.clone()
@@ -490,7 +510,9 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4)}
     src_hash = kernel_source_hash()
     key = str(args.config) if args.config != 3 else f"3@{args.prefix}"
-    roof["traffic"] = profiled_traffic(key if p.mask_layout == "bits" else key + ":rows", src_hash)
+    key += ":rows" if p.mask_layout == "rows" else ""
+    key += ":rope" if args.rope else ""
+    roof["traffic"] = profiled_traffic(key, src_hash)
     roof["kernel"] = "vat_stream" if plan["kernel"] == 1 else "vat_tile"
     roof["algorithmic_bytes_per_launch"] = kvb
     roof["algorithmic_flops_per_launch"] = flops
@@ -509,7 +531,8 @@ def main():
         "dtype": {"f32": "f32", "bf16": "bf16"}[p.q_dtype] + ("+e4m3kv" if p.kv_dtype == "e4m3" else ""),
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[args.config].format(p=args.prefix) +
-                   (", sglang full-row byte mask" if p.mask_layout == "rows" else ""),
+                   (", sglang full-row byte mask" if p.mask_layout == "rows" else "") +
+                   (", queries rotated by RoPE at their tree positions" if args.rope else ""),
                    "batch": p.batch, "query_tokens": tokens, "kv_bytes": kvb,
                    "parallelism": "single GPU", "page_pool_copies": copies},
         "kv_read_gbps_step": round(kvb / (ms_per_step * 1e-3) / 1e9, 1),

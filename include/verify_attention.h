@@ -214,6 +214,15 @@ vat_status_t vat_launch_partial(const vat_problem_t* problem, const void* q, con
                                 const int32_t* mask_indptr, float sm_scale, float k_scale,
                                 float v_scale, void* out, float* lse, void* workspace,
                                 size_t workspace_bytes, void* stream);
+/* vat_launch_partial for verify_attention_rope (same q_cos_sin rows). */
+vat_status_t vat_launch_partial_rope(const vat_problem_t* problem, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* kv_indptr, const int32_t* kv_indices,
+                                     const int32_t* last_page_len, const int32_t* qo_indptr,
+                                     const uint8_t* mask, const int32_t* mask_indptr,
+                                     const float* q_cos_sin, float sm_scale, float k_scale,
+                                     float v_scale, void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 vat_status_t vat_launch_merge(const vat_problem_t* problem, const int32_t* kv_indptr,
                               const int32_t* last_page_len, const int32_t* qo_indptr,
                               float v_scale, void* out, float* lse, void* workspace,

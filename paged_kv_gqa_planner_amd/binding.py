@@ -79,6 +79,8 @@ def load(path: Optional[str] = None):
     lib.vat_launch_merge.argtypes = [P(VatProblem), vp, vp, vp, f, vp, vp, vp, ctypes.c_size_t, vp]
     lib.verify_attention_rope.argtypes = full[:10] + [vp] + full[10:]
     lib.verify_attention_rope.restype = ctypes.c_int
+    lib.vat_launch_partial_rope.argtypes = full[:10] + [vp] + full[10:]
+    lib.vat_launch_partial_rope.restype = ctypes.c_int
     lib.vat_append_kv_rope.argtypes = [P(VatProblem), ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp,
                                        vp, vp, f, f, vp]
     lib.vat_append_kv_rope.restype = ctypes.c_int
@@ -321,14 +323,15 @@ class PreparedAppend:
     """vat_append_kv with every argument fixed (checked once), for timing."""
 
     def __init__(self, k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
-                 qo_indptr, k_scale=1.0, v_scale=1.0, max_qo_len=None, stream=None, num_cus=0):
+                 qo_indptr, k_scale=1.0, v_scale=1.0, max_qo_len=None, stream=None, num_cus=0,
+                 k_cos_sin=None):
         self.lib = load()
         self.keep = (k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
-                     qo_indptr)
+                     qo_indptr, k_cos_sin)
         self.problem, self.args, rope = _append_args(k_new, v_new, k_cache, v_cache, kv_indptr,
                                                      kv_indices, last_page_len, qo_indptr,
                                                      k_scale, v_scale, max_qo_len, stream,
-                                                     num_cus)
+                                                     num_cus, k_cos_sin)
         self.fn = self.lib.vat_append_kv_rope if rope else self.lib.vat_append_kv
 
     def __call__(self):
@@ -345,14 +348,15 @@ class PreparedCall:
     def __init__(self, q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr,
                  mask=None, mask_indptr=None, sm_scale=None, k_scale=1.0, v_scale=1.0,
                  max_qo_len=None, out=None, lse=None, workspace=None, chunk_keys=-1, num_cus=0,
-                 stream=None, mask_layout="bits"):
+                 stream=None, mask_layout="bits", q_cos_sin=None):
         self.lib = load()
         (self.problem, self.sm, self.out, self.lse, self.workspace,
          self.ws_bytes) = _prepare(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
                                    qo_indptr, mask, mask_indptr, sm_scale, max_qo_len, out, lse,
-                                   workspace, chunk_keys, num_cus, mask_layout)
+                                   workspace, chunk_keys, num_cus, mask_layout, q_cos_sin)
         self.keep = (q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr, mask,
-                     mask_indptr)
+                     mask_indptr, q_cos_sin)
+        self.rope = q_cos_sin is not None
         self.k_scale = float(k_scale)
         self.v_scale = float(v_scale)
         self.stream = _stream_handle(stream)
@@ -362,16 +366,23 @@ class PreparedCall:
                      _ptr(mask), _ptr(mask_indptr), self.sm, self.k_scale, self.v_scale,
                      _ptr(self.out), _ptr(self.lse), _ptr(self.workspace), self.ws_bytes,
                      self.stream)
+        self.rope_args = self.args[:10] + (_ptr(q_cos_sin),) + self.args[10:]
         self.merge_args = (ctypes.byref(self.problem), _ptr(kv_indptr), _ptr(last_page_len),
                            _ptr(qo_indptr), self.v_scale, _ptr(self.out), _ptr(self.lse),
                            _ptr(self.workspace), self.ws_bytes, self.stream)
 
     def __call__(self):
-        _check(self.lib.verify_attention(*self.args), "verify_attention")
+        if self.rope:
+            _check(self.lib.verify_attention_rope(*self.rope_args), "verify_attention_rope")
+        else:
+            _check(self.lib.verify_attention(*self.args), "verify_attention")
         return self.out, self.lse
 
     def partial(self):
-        _check(self.lib.vat_launch_partial(*self.args), "vat_launch_partial")
+        if self.rope:
+            _check(self.lib.vat_launch_partial_rope(*self.rope_args), "vat_launch_partial_rope")
+        else:
+            _check(self.lib.vat_launch_partial(*self.args), "vat_launch_partial")
 
     def merge(self):
         _check(self.lib.vat_launch_merge(*self.merge_args), "vat_launch_merge")

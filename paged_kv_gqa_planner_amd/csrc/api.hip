@@ -296,6 +296,24 @@ vat_status_t vat_launch_partial(const vat_problem_t* problem, const void* q, con
                         lse, workspace, (hipStream_t)stream);
 }
 
+vat_status_t vat_launch_partial_rope(const vat_problem_t* problem, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* kv_indptr, const int32_t* kv_indices,
+                                     const int32_t* last_page_len, const int32_t* qo_indptr,
+                                     const uint8_t* mask, const int32_t* mask_indptr,
+                                     const float* q_cos_sin, float sm_scale, float k_scale,
+                                     float v_scale, void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  vat_plan_t plan;
+  vat_status_t st = prepare(problem, q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
+                            qo_indptr, mask, mask_indptr, q_cos_sin, sm_scale, k_scale, v_scale,
+                            out, lse, workspace, workspace_bytes, &plan);
+  if (st != VAT_OK || plan_is_empty(plan)) return st;
+  return launch_partial(problem, plan, q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
+                        qo_indptr, mask, mask_indptr, q_cos_sin, sm_scale, k_scale, v_scale, out,
+                        lse, workspace, (hipStream_t)stream);
+}
+
 vat_status_t vat_launch_merge(const vat_problem_t* problem, const int32_t* kv_indptr,
                               const int32_t* last_page_len, const int32_t* qo_indptr,
                               float v_scale, void* out, float* lse, void* workspace,

@@ -508,30 +508,33 @@ struct RowSet {
     for (int rt = 0; rt < RT; ++rt) {
       if constexpr (ROPE) {
         // x' = x c - y s, y' = y c + x s for the pair (x at step ks, y at step
-        // ks + D / 64, same element), rounded back to bf16.
+        // ks + D / 64, same element), two elements (one word) at a time; the
+        // result is kept as bf16 hi plus bf16 lo (about 2^-17 relative; hi
+        // alone would be 2^-9), both rounded to nearest even by the packed
+        // conversion.
 #pragma unroll
         for (int ks = 0; ks < D / 64; ++ks)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            unsigned& wx = qf[rt][4 * ks + e / 2];
-            unsigned& wy = qf[rt][4 * (ks + D / 64) + e / 2];
-            const int sh = 16 * (e & 1);
-            const float x = __builtin_bit_cast(float, ((wx >> sh) & 0xffffu) << 16);
-            const float y = __builtin_bit_cast(float, ((wy >> sh) & 0xffffu) << 16);
-            const float c = __builtin_bit_cast(float, csr[rt][ks * 16 + e]);
-            const float sn = __builtin_bit_cast(float, csr[rt][ks * 16 + 8 + e]);
-            const float rx = x * c - y * sn, ry = y * c + x * sn;
-            const unsigned nx = f32_to_bf16_bits(rx), ny = f32_to_bf16_bits(ry);
-            // The rotated value split into two bf16 terms: rx ~ hi + lo to
-            // about 2^-17 relative (hi alone would be 2^-9).
-            const unsigned lx = f32_to_bf16_bits(rx - __builtin_bit_cast(float, nx << 16));
-            const unsigned ly = f32_to_bf16_bits(ry - __builtin_bit_cast(float, ny << 16));
-            wx = (wx & ~(0xffffu << sh)) | (nx << sh);
-            wy = (wy & ~(0xffffu << sh)) | (ny << sh);
-            unsigned& lwx = qlo[rt][4 * ks + e / 2];
-            unsigned& lwy = qlo[rt][4 * (ks + D / 64) + e / 2];
-            lwx = (lwx & ~(0xffffu << sh)) | (lx << sh);
-            lwy = (lwy & ~(0xffffu << sh)) | (ly << sh);
+          for (int k = 0; k < 4; ++k) {
+            unsigned& wx = qf[rt][4 * ks + k];
+            unsigned& wy = qf[rt][4 * (ks + D / 64) + k];
+            const float x0 = __builtin_bit_cast(float, wx << 16);
+            const float x1 = __builtin_bit_cast(float, wx & 0xffff0000u);
+            const float y0 = __builtin_bit_cast(float, wy << 16);
+            const float y1 = __builtin_bit_cast(float, wy & 0xffff0000u);
+            const float c0 = __builtin_bit_cast(float, csr[rt][ks * 16 + 2 * k]);
+            const float c1 = __builtin_bit_cast(float, csr[rt][ks * 16 + 2 * k + 1]);
+            const float s0 = __builtin_bit_cast(float, csr[rt][ks * 16 + 8 + 2 * k]);
+            const float s1 = __builtin_bit_cast(float, csr[rt][ks * 16 + 8 + 2 * k + 1]);
+            const float rx0 = __builtin_fmaf(x0, c0, -y0 * s0), rx1 = __builtin_fmaf(x1, c1, -y1 * s1);
+            const float ry0 = __builtin_fmaf(y0, c0, x0 * s0), ry1 = __builtin_fmaf(y1, c1, x1 * s1);
+            const unsigned hx = cvt_pk_bf16(rx0, rx1), hy = cvt_pk_bf16(ry0, ry1);
+            qlo[rt][4 * ks + k] = cvt_pk_bf16(rx0 - __builtin_bit_cast(float, hx << 16),
+                                              rx1 - __builtin_bit_cast(float, hx & 0xffff0000u));
+            qlo[rt][4 * (ks + D / 64) + k] = cvt_pk_bf16(ry0 - __builtin_bit_cast(float, hy << 16),
+                                                         ry1 - __builtin_bit_cast(float, hy & 0xffff0000u));
+            wx = hx;
+            wy = hy;
           }
       }
       if (!row_ok[rt]) {
