@@ -190,8 +190,10 @@ vat_status_t verify_attention(const vat_problem_t* problem, const void* q, const
  * aligned; row r holds cos(th_0) .. cos(th_{D/2-1}), sin(th_0) ..
  * sin(th_{D/2-1}) of query token r's position. Query row r is rotated LLaMA
  * style -- dimension i pairs with i + D/2: q'_i = q_i c_i - q_{i+D/2} s_i,
- * q'_{i+D/2} = q_{i+D/2} c_i + q_i s_i -- in float32 and rounded to bf16
- * before the products. Cached keys are used as stored: a cache written with
+ * q'_{i+D/2} = q_{i+D/2} c_i + q_i s_i -- in float32 with fused
+ * multiply-adds; the rotated row enters the products as the sum of two bf16
+ * rows (its bf16 rounding, then the bf16 rounding of what remains), about 16
+ * significant bits. Cached keys are used as stored: a cache written with
  * vat_append_kv_rope holds rotated keys. problem->rope must be 1. */
 vat_status_t verify_attention_rope(const vat_problem_t* problem, const void* q,
                                    const void* k_cache, const void* v_cache,

@@ -68,9 +68,11 @@ __global__ __launch_bounds__(kMergeThreads) void vat_merge(MergeArgs a) {
       v[0] = po[0];
     }
   };
+  // Only rows that exist are requested (n is wave-uniform).
   float v0[U][PER];
 #pragma unroll
-  for (int u = 0; u < U; ++u) load_row(min(u, n - 1), v0[u]);
+  for (int u = 0; u < U; ++u)
+    if (u < n) load_row(u, v0[u]);
   const float ls0 = lane < n ? a.part_lse[slot(lane)] : kNegInf;
   float m = ls0;
   for (int i = lane + 64; i < n; i += 64) m = fmaxf(m, a.part_lse[slot(i)]);
@@ -93,20 +95,21 @@ __global__ __launch_bounds__(kMergeThreads) void vat_merge(MergeArgs a) {
       const bool first = base == 0 && j0 == 0;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int j = min(j0 + u, cnt - 1);
-        wj[u] = j0 + u < cnt ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j))
-                             : 0.f;
+        if (j0 + u >= cnt) break;
+        wj[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j0 + u));
         if (first) {
 #pragma unroll
           for (int k = 0; k < PER; ++k) v[u][k] = v0[u][k];
         } else {
-          load_row(base + j, v[u]);
+          load_row(base + j0 + u, v[u]);
         }
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u) {
+        if (j0 + u >= cnt) break;
 #pragma unroll
         for (int k = 0; k < PER; ++k) o[k] += wj[u] * v[u][k];
+      }
     }
   }
   den = wave_sum(den);
