@@ -158,6 +158,9 @@ typedef struct {
                                1 (streaming kernel, more than one row block):
                                one-dimensional grid in which the row blocks of
                                each (work item, KV head) run on one XCD */
+  int32_t merge_rows;       /* query rows per merge workgroup: 4 (one wave per
+                               row, for requests with many partials) or 16
+                               (four rows per wave); 0 when direct */
 } vat_plan_t;
 
 /* Plan a call: validates the shapes and fills *plan. Host only; touches the

@@ -36,7 +36,8 @@ class VatPlan(ctypes.Structure):
         "direct", "kernel", "stages", "slices", "group", "rows", "row_tiles_per_wave", "waves_rows", "waves_keys", "dma_waves",
         "rows_per_block", "row_blocks", "chunk_keys", "num_chunk_ids", "grid_x", "grid_y",
         "threads", "lds_bytes", "merge_grid", "merge_threads", "num_cus")] + [
-        ("workspace_bytes", ctypes.c_int64), ("block_order", ctypes.c_int32)]
+        ("workspace_bytes", ctypes.c_int64), ("block_order", ctypes.c_int32),
+        ("merge_rows", ctypes.c_int32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

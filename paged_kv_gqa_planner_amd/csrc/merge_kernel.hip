@@ -3,21 +3,31 @@
 // normalised output is weighted by its share of the softmax mass,
 // w_i = 2^(lse_i - max lse), and the merged lse is max + log2(sum w).
 //
-// One wave per query row (each lane owns D / 64 head dims), four rows per
-// workgroup: the partials' lse give their max and weights, then the weighted
-// sum of their rows is formed. A request's partials
-// are its chunks (ids from chunk_start) or, with balanced slices of the
-// page-index space, the slices x_lo .. x_hi its pages fall in (slot x + b). Requests that fit one chunk or
-// slice were written directly by the partial kernel and are skipped.
+// A request's partials are its chunks (ids from chunk_start) or, with
+// balanced slices of the page-index space, the slices x_lo .. x_hi its pages
+// fall in (slot x + b). Requests that fit one chunk or slice were written
+// directly by the partial kernel and are skipped.
 #include "device_common.h"
 
 namespace vat {
 
-template <int QF32, int D>
+// Sixteen lanes own one row's D head dims, D / 16 consecutive dims each, so
+// one partial row is two (D 128) or one 16-byte load per lane. Without SPLIT
+// a wave merges four rows (requests with few partials); with SPLIT it merges
+// one row and its four 16-lane groups take every fourth partial, so up to 4 U
+// partials arrive in one round of loads, and the groups combine at the end.
+// Every lane reads the lse values of its own partials (the 16 lanes of a
+// group share each address), so the weights need no cross-lane traffic; a
+// row with more partials than one round holds takes several rounds, combined
+// with a running max that rescales what came before.
+template <int QF32, int D, bool SPLIT>
 __global__ __launch_bounds__(kMergeThreads) void vat_merge(MergeArgs a) {
-  constexpr int PER = D / 64;  // head dims per lane
+  constexpr int PER = D / 16;  // head dims per lane: 8 or 4
+  constexpr int U = 64 / PER;  // partials per lane per round: 8 or 16
+  constexpr int STEP = SPLIT ? 4 : 1;
+  constexpr int ROWS = SPLIT ? kMergeThreads / 64 : kMergeThreads / 16;  // rows per workgroup
   const int lane = threadIdx.x & 63;
-  const int lr = threadIdx.x >> 6;  // row within the group
+  const int sub = lane >> 4, l16 = lane & 15;
   int x = blockIdx.x;
   const int rg = x % a.row_groups;
   x /= a.row_groups;
@@ -25,111 +35,117 @@ __global__ __launch_bounds__(kMergeThreads) void vat_merge(MergeArgs a) {
   x /= a.row_blocks;
   const int h = x % a.hkv;
   const int b = x / a.hkv;
-  Req r;
+  const Req r = make_req(a.kv_indptr[b], a.kv_indptr[b + 1], a.last_page_len[b], a.qo_indptr[b],
+                         a.qo_indptr[b + 1], 0, a.page_shift, a.num_kv_indices, a.tokens);
   int n, first;  // partials of request b: slots first + i, i < n
   if (a.slices > 0) {
-    // Slices of the page-index space, `per` pages each: request b's pages
-    // [kv_indptr[b], kv_indptr[b + 1]) fall in slices x_lo .. x_hi.
-    r = make_req(a.kv_indptr[b], a.kv_indptr[b + 1], a.last_page_len[b], a.qo_indptr[b],
-                 a.qo_indptr[b + 1], 0, a.page_shift, a.num_kv_indices, a.tokens);
+    // Slices of `per` pages: request b's pages [kv_indptr[b], kv_indptr[b + 1])
+    // fall in slices x_lo .. x_hi.
     if (r.L == 0 || r.pages == 0) return;
     const int per = (a.num_kv_indices + a.slices - 1) / a.slices;
     const int x_lo = r.kv_start / per;
-    const int x_hi = (r.kv_start + r.pages - 1) / per;
-    n = x_hi - x_lo + 1;
+    n = (r.kv_start + r.pages - 1) / per - x_lo + 1;
     first = x_lo + b;
   } else {
-    r = make_req(a.kv_indptr[b], a.kv_indptr[b + 1], a.last_page_len[b], a.qo_indptr[b],
-                 a.qo_indptr[b + 1], 0, a.page_shift, a.num_kv_indices, a.tokens);
     n = chunk_count(r.kv_len, a.chunk_keys);
     first = chunk_start(r.kv_start, a.page_shift, a.chunk_keys, b);
   }
   if (n <= 1) return;  // written directly by the partial kernel
-  const int local = rg * kMergeRows + lr;
+  const int local = rg * ROWS + (SPLIT ? (int)(threadIdx.x >> 6) : (int)(threadIdx.x >> 4));
   const int row = rb * a.rows_per_block + local;
-  if (local >= a.rows_per_block || row >= a.group * r.L) return;
-  const int t = row / a.group, g = row % a.group;
+  const bool ok = local < a.rows_per_block && row < a.group * r.L;
+  if (!__ballot(ok)) return;
+  const int ph = SPLIT ? sub : 0;  // this lane group's first partial
   auto slot = [&](int i) -> long long {
     const int cid = min(first + i, a.num_ids - 1);
     return (((long long)cid * a.hkv + h) * a.row_blocks + rb) * a.rows_per_block + local;
   };
-
-  // The first U partial rows are requested together with every partial's
-  // base-2 lse (lane i holds partials i, i + 64, ...), so a request with up
-  // to U partials costs one round of loads after its geometry.
-  constexpr int U = 16;
-  auto load_row = [&](int i, float (&v)[PER]) {
-    const float* po = a.part_o + slot(i) * D + lane * PER;
-    if constexpr (PER == 2) {
-      const float2 x2 = *(const float2*)po;
-      v[0] = x2.x;
-      v[1] = x2.y;
-    } else {
-      v[0] = po[0];
-    }
-  };
-  // Only rows that exist are requested (n is wave-uniform).
-  float v0[U][PER];
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-    if (u < n) load_row(u, v0[u]);
-  const float ls0 = lane < n ? a.part_lse[slot(lane)] : kNegInf;
-  float m = ls0;
-  for (int i = lane + 64; i < n; i += 64) m = fmaxf(m, a.part_lse[slot(i)]);
-  m = wave_max(m);
-  const float mb = (m == kNegInf) ? 0.f : m;
-  // Weights w_i = 2^(lse_i - max) (0 for an empty partial) and the weighted
-  // sum of the rows; rows past the first U are requested U at a time.
-  float den = 0.f;
   float o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
-  for (int base = 0; base < n; base += 64) {
-    const int i = base + lane;
-    const float lsi = base == 0 ? ls0 : (i < n ? a.part_lse[slot(i)] : kNegInf);
-    const float w = fast_exp2(lsi - mb);
-    den += w;
-    const int cnt = min(64, n - base);
-    for (int j0 = 0; j0 < cnt; j0 += U) {
-      float v[U][PER], wj[U];
-      const bool first = base == 0 && j0 == 0;
+  float m = kNegInf, den = 0.f;
+  for (int i0 = 0; i0 < n; i0 += U * STEP) {
+    float ls[U];
+    f32x4 v[U][PER / 4];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (j0 + u >= cnt) break;
-        wj[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j0 + u));
-        if (first) {
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + ph + u * STEP;
+      ls[u] = kNegInf;
+      if (i < n && ok) {
+        const long long sl = slot(i);
+        ls[u] = a.part_lse[sl];
+        const f32x4* po = (const f32x4*)(a.part_o + sl * D + l16 * PER);
 #pragma unroll
-          for (int k = 0; k < PER; ++k) v[u][k] = v0[u][k];
-        } else {
-          load_row(base + j0 + u, v[u]);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (j0 + u >= cnt) break;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) o[k] += wj[u] * v[u][k];
+        for (int k = 0; k < PER / 4; ++k) v[u][k] = po[k];
       }
     }
+    float mn = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mn = fmaxf(mn, ls[u]);
+    const float base = (mn == kNegInf) ? 0.f : mn;
+    const float sc = fast_exp2(m - base);
+    den *= sc;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o[k] *= sc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ls[u] == kNegInf) continue;  // absent, or an empty partial: adds nothing
+      const float w = fast_exp2(ls[u] - base);
+      den += w;
+#pragma unroll
+      for (int k = 0; k < PER / 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[4 * k + e] += w * v[u][k][e];
+    }
+    m = mn;
   }
-  den = wave_sum(den);
+  if constexpr (SPLIT) {
+    // The four lane groups hold disjoint partials of the same row.
+    float mall = fmaxf(m, __shfl_xor(m, 16));
+    mall = fmaxf(mall, __shfl_xor(mall, 32));
+    const float base = (mall == kNegInf) ? 0.f : mall;
+    const float sc = fast_exp2(m - base);
+    den *= sc;
+    den += __shfl_xor(den, 16);
+    den += __shfl_xor(den, 32);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      o[k] *= sc;
+      o[k] += __shfl_xor(o[k], 16);
+      o[k] += __shfl_xor(o[k], 32);
+    }
+    m = mall;
+    if (sub != 0) return;
+  }
+  if (!ok) return;
+  const int t = row / a.group, g = row % a.group;
   const long long orow = (long long)(r.q_start + t) * a.hq + h * a.group + g;
   const float sc = den > 0.f ? a.v_scale / den : 0.f;
   if constexpr (QF32) {
-    float* op = (float*)a.out + orow * D + lane * PER;
+    f32x4* op = (f32x4*)((float*)a.out + orow * D + l16 * PER);
 #pragma unroll
-    for (int k = 0; k < PER; ++k) op[k] = o[k] * sc;
+    for (int k = 0; k < PER / 4; ++k)
+      op[k] = f32x4{o[4 * k] * sc, o[4 * k + 1] * sc, o[4 * k + 2] * sc, o[4 * k + 3] * sc};
   } else {
-    unsigned short* op = (unsigned short*)a.out + orow * D + lane * PER;
-    if constexpr (PER == 2) *(unsigned*)op = pack_bf16x2(o[0] * sc, o[1] * sc);
-    else op[0] = (unsigned short)f32_to_bf16_bits(o[0] * sc);
+    unsigned short* op = (unsigned short*)a.out + orow * D + l16 * PER;
+    if constexpr (PER == 8) {
+      *(u32x4*)op = u32x4{pack_bf16x2(o[0] * sc, o[1] * sc), pack_bf16x2(o[2] * sc, o[3] * sc),
+                          pack_bf16x2(o[4] * sc, o[5] * sc), pack_bf16x2(o[6] * sc, o[7] * sc)};
+    } else {
+      *(u32x2*)op = u32x2{pack_bf16x2(o[0] * sc, o[1] * sc), pack_bf16x2(o[2] * sc, o[3] * sc)};
+    }
   }
-  if (lane == 0) a.lse[orow] = den > 0.f ? (mb + fast_log2(den)) * kLn2 : kNegInf;
+  if (l16 == 0) a.lse[orow] = den > 0.f ? (m + fast_log2(den)) * kLn2 : kNegInf;
 }
 
-const void* merge_kernel(int q_is_f32, int head_dim) {
-  if (q_is_f32) return (const void*)(head_dim == 64 ? vat_merge<1, 64> : vat_merge<1, 128>);
-  return (const void*)(head_dim == 64 ? vat_merge<0, 64> : vat_merge<0, 128>);
+// rows_per_workgroup: kMergeRows (one row per wave, SPLIT) or kMergeRows4.
+const void* merge_kernel(int q_is_f32, int head_dim, int rows_per_workgroup) {
+  if (rows_per_workgroup == kMergeRows4) {
+    if (q_is_f32) return (const void*)(head_dim == 64 ? vat_merge<1, 64, false> : vat_merge<1, 128, false>);
+    return (const void*)(head_dim == 64 ? vat_merge<0, 64, false> : vat_merge<0, 128, false>);
+  }
+  if (q_is_f32) return (const void*)(head_dim == 64 ? vat_merge<1, 64, true> : vat_merge<1, 128, true>);
+  return (const void*)(head_dim == 64 ? vat_merge<0, 64, true> : vat_merge<0, 128, true>);
 }
 
 }  // namespace vat

@@ -69,6 +69,13 @@ vat_status_t validate_append(const vat_problem_t* p, int32_t src_dtype) {
   return VAT_OK;
 }
 
+// Query rows per merge workgroup: four per wave (16 lanes a row) when a
+// request's partials fit one round of that kernel's loads, else one per wave.
+static int32_t merge_rows_for(int64_t partials, int64_t head_dim) {
+  const int64_t per_round = head_dim == 128 ? 8 : 16;
+  return partials <= per_round ? kMergeRows4 : kMergeRows;
+}
+
 vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan) {
   if (!plan) return VAT_ERR_NULL;
   vat_status_t st = validate_problem(p);
@@ -224,7 +231,9 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
     plan->grid_x = int32_t(nx);
     plan->grid_y = int32_t(p->num_kv_heads * RB);
     if (plan->direct) return VAT_OK;
-    const int64_t row_groups = cdiv(M, kMergeRows);
+    // A request's pages span about nx / B + 1 slices.
+    plan->merge_rows = merge_rows_for(nx / p->batch + 1, D);
+    const int64_t row_groups = cdiv(M, plan->merge_rows);
     plan->merge_grid = int32_t(base_items * row_groups);
     const int64_t parts = (nx + p->batch) * p->num_kv_heads * RB;
     const int64_t lse_off = cdiv(parts * M * D * 4, 256) * 256;
@@ -254,7 +263,9 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
     plan->workspace_bytes = 0;
     return VAT_OK;
   }
-  const int64_t row_groups = cdiv(M, kMergeRows);
+  // A request of average length has about total_keys / (B C) + 1 chunks.
+  plan->merge_rows = merge_rows_for(total_keys / (int64_t(p->batch) * ck) + 1, D);
+  const int64_t row_groups = cdiv(M, plan->merge_rows);
   const int64_t mg = base_items * row_groups;
   if (mg > int64_t(INT32_MAX)) return VAT_ERR_UNSUPPORTED;
   plan->merge_grid = int32_t(mg);

@@ -27,8 +27,10 @@ constexpr int kStreamMaxTiles = 16;
 constexpr int kStreamLdsBudget = 128 * 1024;
 // Page ids the streaming kernel keeps in LDS at a time.
 constexpr int kStreamPageWindow = 2048;
-// Query rows merged per merge-kernel workgroup (one wave per row).
+// Query rows merged per merge-kernel workgroup: one wave per row, or four
+// rows per wave.
 constexpr int kMergeRows = 4;
+constexpr int kMergeRows4 = 16;
 constexpr int kMergeThreads = 256;
 // Chunk lengths the planner picks are multiples of kChunkQuantum within
 // [kMinChunkKeys, kMaxChunkKeys].

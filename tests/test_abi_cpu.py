@@ -43,7 +43,7 @@ def test_library_exports_every_header_function(lib):
             "vat_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.vat_abi_version() == 2
+    assert lib.vat_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -111,6 +111,12 @@ def test_plans_for_the_workloads(lib, cid):
         parts = plan.num_chunk_ids * p.num_kv_heads * plan.row_blocks
         assert plan.workspace_bytes >= parts * plan.rows_per_block * (p.head_dim + 1) * 4
         assert plan.merge_grid > 0
+        # Few partials per request: four rows per merge wave.
+        assert plan.merge_rows == (4 if cid == 3 else 16)
+        groups = plan.merge_grid // (p.batch * p.num_kv_heads * plan.row_blocks)
+        assert groups == -(-plan.rows_per_block // plan.merge_rows)
+    else:
+        assert plan.merge_rows == 0
 
 
 def test_plan_is_shape_only_and_deterministic(lib):
