@@ -628,6 +628,18 @@ __device__ __forceinline__ void wait_lds_writes() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
+// Workgroup barrier for hand-offs through LDS: the caller's LDS writes are
+// complete first, while its global loads and stores (and the DMA waves' stage
+// loads) stay in flight -- __syncthreads would wait for those too, draining
+// the stage ring. The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  wait_lds_writes();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int D, int RT>
 __device__ __forceinline__ void store_pair_state(const StreamAcc<D, RT>& acc, float* slot, int lane) {
   constexpr int NDT = D / 16;
@@ -826,7 +838,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   // chunk's page ids.
   if (computes && nst_all > 0) start_segment(seg_of(0));
   if (a.slices == 0) fill_window(win, a, w0, 0, wcount);
-  __syncthreads();  // page window written
+  lds_barrier();  // page window written; the first segment's query rows stay in flight
   if (nst_all == 0) return;
 
   // ---- DMA issue of global stage g into ring buffer `buf`. Every wave runs
@@ -895,7 +907,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
       float lrow[RT];
       if constexpr (P == 2) {
         if (computes && has_rows && phase == 1) store_pair_state<D, RT>(acc, pair_slot, lane);
-        __syncthreads();
+        lds_barrier();  // not __syncthreads: the DMA waves keep their stages in flight
         if (computes && has_rows && phase == 0) merge_pair_state<D, RT>(acc, lrow, pair_slot, true, lane);
       } else {
 #pragma unroll
