@@ -173,6 +173,20 @@ struct Vis {
 // selects that would run on every stage.
 __device__ __forceinline__ void keep_branch() { asm volatile(""); }
 
+// Visibility of keys c = 0..63 of a stage to one query row, as a bit mask:
+// key c has draft index d + c (negative: a prefix key, always visible; 0..63:
+// bit d + c of the row's draft bits; beyond: no draft) and must satisfy
+// c <= lim (inside the item).
+__device__ __forceinline__ unsigned long long visible_bits(unsigned long long bits, int d, int lim) {
+  unsigned long long w;
+  if (d >= 64) w = 0ull;
+  else if (d >= 0) w = bits >> d;
+  else if (d > -64) w = (bits << (-d)) | ((1ull << (-d)) - 1ull);
+  else w = ~0ull;
+  const unsigned long long in = lim >= 63 ? ~0ull : (lim < 0 ? 0ull : (2ull << lim) - 1ull);
+  return w & in;
+}
+
 // One 64-key stage against this wave's RT row tiles. The four 16-key tiles
 // are processed together: their S^T MFMAs interleave, the softmax takes one
 // row max over all 64 keys, and the V^T reads of tile kt + 1 are in flight
@@ -241,22 +255,37 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
   if (n_last >= vis.hi ||
       (n_last >= vis.masked_from && (vis.has_mask || n_last - vis.masked_from > vis.t_min))) {
     keep_branch();
+    // One compare (causal) or one bit test (mask) and one select per logit,
+    // no control flow. This lane's logit (kt, e) is key nb + c, c = 16 kt + e.
+    const int nb = n0 + 16 * kt0 + 4 * j4;
+    const int lim_in = vis.hi - 1 - nb;   // c <= lim_in: inside the item
+    const int d0 = nb - vis.masked_from;  // draft index of c = 0 (negative: a prefix key)
+    if (vis.has_mask) {
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+      for (int rt = 0; rt < RT; ++rt) {
+        const unsigned long long w0 = visible_bits(row_bits[rt], d0, lim_in);
+        const unsigned long long w1 = KT > 4 ? visible_bits(row_bits[rt], d0 + 64, lim_in - 64) : 0ull;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int n = n0 + 16 * (kt0 + kt) + 4 * j4 + e;
-        const int jd = n - vis.masked_from;
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          bool ok = n < vis.hi;
-          if (jd >= 0) {
-            if (vis.has_mask) ok = ok && jd < 64 && ((row_bits[rt] >> jd) & 1ull);
-            else ok = ok && jd <= row_t[rt];
+          for (int e = 0; e < 4; ++e) {
+            const int c = 16 * kt + e;
+            const bool ok = (((c < 64 ? w0 : w1) >> (c & 63)) & 1ull) != 0ull;
+            st[kt][rt][e] = ok ? st[kt][rt][e] : kNegInf;
           }
-          if (!ok) st[kt][rt][e] = kNegInf;
-        }
       }
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        // jd <= t  <=>  c <= t - d0 (row tokens are >= 0, so prefix keys pass)
+        const int lim = min(lim_in, row_t[rt] - d0);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            st[kt][rt][e] = (16 * kt + e <= lim) ? st[kt][rt][e] : kNegInf;
+      }
+    }
   }
   // ---- online softmax (base 2); p replaces the logits. The running max is
   // raised only when the stage's max exceeds it by more than kRescaleSlack,
