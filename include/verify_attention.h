@@ -157,7 +157,11 @@ typedef struct {
   int32_t block_order;      /* 0: partial grid (num_chunk_ids, Hkv * row_blocks);
                                1 (streaming kernel, more than one row block):
                                one-dimensional grid in which the row blocks of
-                               each (work item, KV head) run on one XCD */
+                               each (work item, KV head) run on one XCD, one
+                               workgroup per row block;
+                               2: as 1, but each workgroup runs two row blocks
+                               of its (work item, KV head), RB - 1 - k and k,
+                               ceil(row_blocks / 2) workgroups per group */
   int32_t merge_rows;       /* query rows per merge workgroup: 4 (one wave per
                                row, for requests with many partials) or 16
                                (four rows per wave); 0 when direct */

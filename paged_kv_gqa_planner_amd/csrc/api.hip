@@ -397,6 +397,6 @@ const char* vat_status_string(vat_status_t status) {
   return "unknown status";
 }
 
-int32_t vat_abi_version(void) { return 3; }
+int32_t vat_abi_version(void) { return 4; }
 
 }  // extern "C"

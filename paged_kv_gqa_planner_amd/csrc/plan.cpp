@@ -250,11 +250,19 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   plan->grid_y = int32_t(p->num_kv_heads * RB);
   if (stream && RB > 1) {
     // Row blocks re-read their group's keys: keep each group's blocks on one
-    // XCD (one L2), eight groups per round (one-dimensional grid).
+    // XCD (one L2), eight groups per round (one-dimensional grid). With eight
+    // or more row blocks per CU, pair them (block order 2): a workgroup runs
+    // its group's blocks RB - 1 - k and k back to back, so half as many
+    // workgroups pay the start-up and the causal work per workgroup evens
+    // out. Both blocks restart at the item's first key, so the item's pages
+    // must fit the page window.
     const int64_t groups = ids * p->num_kv_heads;
-    const int64_t g1 = 8 * RB * cdiv(groups, 8);
+    const bool pair = groups * RB >= 8 * int64_t(num_cus) &&
+                      cdiv(ck, p->page_size) + 1 <= kStreamPageWindow;
+    const int64_t w = pair ? cdiv(RB, 2) : RB;
+    const int64_t g1 = 8 * w * cdiv(groups, 8);
     if (g1 > int64_t(INT32_MAX)) return VAT_ERR_UNSUPPORTED;
-    plan->block_order = 1;
+    plan->block_order = pair ? 2 : 1;
     plan->grid_x = int32_t(g1);
     plan->grid_y = 1;
   }

@@ -435,6 +435,7 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
 struct SegLane {
   int lo = 0, hi = 0, nst = 0, incl = 0;
   int woff = 0, q_start = 0, L = 0, prefix = 0, mask_off = 0, slot = 0, whole = 0;
+  int rb = 0;  // row block of the segment's rows
 };
 
 __device__ __forceinline__ int lane_val(int v, int i) { return __builtin_amdgcn_readlane(v, i); }
@@ -724,18 +725,25 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   // Row blocks of one KV head are dispatched longest first (under a causal
-  // limit a later block reaches more keys). In block order 1 the grid is one-
-  // dimensional: workgroup L runs on XCD L % 8, and the row blocks of group
-  // q = (work item, KV head) take workgroups (q % 8) + 8 (RB (q / 8) + r), so
+  // limit a later block reaches more keys). In block orders 1 and 2 the grid
+  // is one-dimensional: workgroup L runs on XCD L % 8, and the W workgroups
+  // of group q = (work item, KV head) are (q % 8) + 8 (W (q / 8) + k), so
   // they share that XCD's L2 and start within one round of eight groups.
-  int item, h, rb;
+  // Order 1: W = RB, workgroup k takes block RB - 1 - k. Order 2 (many
+  // blocks): W = ceil(RB / 2), workgroup k takes blocks RB - 1 - k and k as
+  // two segments of one ring -- half the workgroups pay the start-up, and the
+  // longest causal block shares a workgroup with the shortest.
+  int item, h, rb, rb2 = -1;
   if (a.block_order) {
     const int L = (int)blockIdx.x;
-    const int q = (L & 7) + 8 * (L / (8 * a.row_blocks));
+    const int W = a.block_order == 2 ? (a.row_blocks + 1) / 2 : a.row_blocks;
+    const int q = (L & 7) + 8 * (L / (8 * W));
     if (q >= a.num_ids * a.hkv) return;
     item = q % a.num_ids;
     h = q / a.num_ids;
-    rb = a.row_blocks - 1 - (L >> 3) % a.row_blocks;
+    const int k = (L >> 3) % W;
+    rb = a.row_blocks - 1 - k;
+    if (a.block_order == 2 && k < rb) rb2 = k;
   } else {
     item = (int)blockIdx.x;
     h = blockIdx.y / a.row_blocks;
@@ -777,6 +785,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
       sg.mask_off = r.mask_off;
       sg.slot = item + lane;
       sg.whole = sg.lo == 0 && sg.hi == r.kv_len;
+      sg.rb = rb;
     }
 #pragma unroll
     for (int k = 0; k < PT; ++k) {
@@ -790,22 +799,32 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
     Req r;
     Item it;
     if (!find_item(ra, item, lane, r, it) || r.L == 0) return;
-    if (rb * a.rows_per_block >= a.group * r.L) return;  // no row of this block exists
     const int lo = it.j * a.chunk_keys;
-    int hi = min(lo + a.chunk_keys, r.kv_len);
+    const int hi_item = min(lo + a.chunk_keys, r.kv_len);
     const bool whole_item = chunk_count(r.kv_len, a.chunk_keys) == 1;
-    if (whole_item && !a.has_mask) {
-      // Causal: no row of this block sees a key past its last row's token.
-      const int t_hi = min(r.L - 1, (rb * a.rows_per_block + a.rows_per_block - 1) / a.group);
-      hi = min(hi, r.prefix + t_hi + 1);
-    }
-    if (lo >= hi) return;
+    // Keys [lo, hi) of row block b; an empty range when no row of the block
+    // exists. Causal: no row of a block sees a key past its last row's token.
+    auto block_hi = [&](int b) {
+      if (b < 0 || b * a.rows_per_block >= a.group * r.L) return lo;
+      if (!whole_item || a.has_mask) return hi_item;
+      const int t_hi = min(r.L - 1, (b * a.rows_per_block + a.rows_per_block - 1) / a.group);
+      return min(hi_item, r.prefix + t_hi + 1);
+    };
+    // Either block may hold no row of this request (shorter requests have
+    // fewer blocks); an empty one is simply no segment.
+    const int hi_a = block_hi(rb), hi_b = block_hi(rb2);
+    const int hi_max = max(hi_a, hi_b);
+    if (lo >= hi_max) return;
     w0 = r.kv_start + (lo >> shift);
-    wcount = ((hi - 1) >> shift) - (lo >> shift) + 1;
-    if (lane == 0) {
+    wcount = ((hi_max - 1) >> shift) - (lo >> shift) + 1;
+    // Lane 0: block rb; lane 1: block rb2 (block order 2). Both restart at
+    // key lo inside the same page window (the planner pairs only items that
+    // fit the window).
+    const int my_hi = lane == 0 ? hi_a : hi_b;
+    if (lane < 2 && my_hi > lo) {
       sg.lo = lo;
-      sg.hi = hi;
-      sg.nst = (hi - lo + SK - 1) / SK;
+      sg.hi = my_hi;
+      sg.nst = (my_hi - lo + SK - 1) / SK;
       sg.woff = r.kv_start - w0;
       sg.q_start = r.q_start;
       sg.L = r.L;
@@ -813,6 +832,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
       sg.mask_off = r.mask_off;
       sg.slot = it.slot;
       sg.whole = whole_item;
+      sg.rb = lane == 0 ? rb : rb2;
     }
   }
   // Global stage numbering: inclusive prefix sum of the stage counts.
@@ -837,8 +857,8 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   const bool computes = wave < ncomp;
   const int tset = wave % a.waves_rows;
   const int phase = wave / a.waves_rows;
-  const int row0 = tset * RT * 16;                  // within the row block
-  const int rbase = rb * a.rows_per_block + row0;   // in the request's rows
+  const int row0 = tset * RT * 16;  // within the row block
+  int rbase = row0;                   // in the request's rows (set per segment)
   float* pair_slot = (float*)(smem + NS * G::STAGE + kStreamPageWindow * 4) + tset * PairSlot<D, RT>::FLOATS;
   RowSet<KV, D, RT, ROWS, ROPE> rs;
   StreamAcc<D, RT> acc;
@@ -846,6 +866,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   bool has_rows = false;
   int seg_L = 0;
   auto start_segment = [&](int s) {
+    rbase = lane_val(sg.rb, s) * a.rows_per_block + row0;
     seg_L = lane_val(sg.L, s);
     has_rows = rbase < a.group * seg_L;
     rs.fetch(a, lane_val(sg.q_start, s), seg_L, lane_val(sg.prefix, s), lane_val(sg.mask_off, s),
@@ -944,7 +965,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
       }
       if (computes && has_rows && phase == 0)
         write_rows<KV, D, RT, ROWS, ROPE>(acc, lrow, rs, a, lane_val(sg.q_start, s), lane_val(sg.whole, s) != 0,
-                              lane_val(sg.slot, s), rb, row0, h, lane);
+                              lane_val(sg.slot, s), lane_val(sg.rb, s), row0, h, lane);
     }
   }
 }

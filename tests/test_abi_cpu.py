@@ -43,7 +43,7 @@ def test_library_exports_every_header_function(lib):
             "vat_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.vat_abi_version() == 3
+    assert lib.vat_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -81,8 +81,9 @@ def test_plans_for_the_workloads(lib, cid):
     assert plan.rows_per_block * plan.row_blocks >= plan.rows
     if plan.block_order:
         groups = plan.num_chunk_ids * p.num_kv_heads
+        w = -(-plan.row_blocks // 2) if plan.block_order == 2 else plan.row_blocks
         assert plan.grid_y == 1
-        assert plan.grid_x == 8 * plan.row_blocks * -(-groups // 8)
+        assert plan.grid_x == 8 * w * -(-groups // 8)
     else:
         assert plan.grid_y == p.num_kv_heads * plan.row_blocks
     if plan.slices:
@@ -151,38 +152,52 @@ def test_forced_chunk_and_direct(lib):
     assert B.vat_workspace_size(base_problem(chunk_keys=48)) == p.workspace_bytes > 0
 
 
-def _decode_block(L, row_blocks, num_ids, hkv):
-    """Host restatement of the streaming kernel's one-dimensional block order:
-    (work item, KV head, row block) of workgroup L, or None for padding."""
-    q = (L & 7) + 8 * (L // (8 * row_blocks))
+def _decode_block(L, row_blocks, num_ids, hkv, order=1):
+    """Host restatement of the streaming kernel's one-dimensional block orders:
+    the (work item, KV head, row block) triples workgroup L runs, in order
+    (block order 2 pairs blocks RB - 1 - k and k), or None for padding."""
+    w = (row_blocks + 1) // 2 if order == 2 else row_blocks
+    q = (L & 7) + 8 * (L // (8 * w))
     if q >= num_ids * hkv:
         return None
-    return q % num_ids, q // num_ids, row_blocks - 1 - (L >> 3) % row_blocks
+    k = (L >> 3) % w
+    blocks = [row_blocks - 1 - k]
+    if order == 2 and k < row_blocks - 1 - k:
+        blocks.append(k)
+    return [(q % num_ids, q // num_ids, rb) for rb in blocks]
 
 
-@pytest.mark.parametrize("cid", [4, 7])
-def test_row_blocks_of_a_group_share_an_xcd(lib, cid):
-    """Workgroup L runs on XCD L % 8. Every (item, head, row block) is launched
+@pytest.mark.parametrize("cid,order", [(4, 2), (7, 1)])
+def test_row_blocks_of_a_group_share_an_xcd(lib, cid, order):
+    """Workgroup L runs on XCD L % 8. Every (item, head, row block) is run
     once, the row blocks of one (item, head) sit on one XCD and are launched
-    within one round of 8 * row_blocks workgroups, the XCDs get equal shares
-    of groups (to one), and a group's longest row block comes first."""
+    within one round of workgroups, the XCDs get equal shares of groups (to
+    one), and a group's longest row block comes first. Prefill (config 4) has
+    enough blocks to pair them (order 2: longest with shortest); the wide tree
+    (config 7) keeps one block per workgroup."""
     p = make_config(cid)
     plan = B.vat_plan(problem_of(p))
-    assert plan.block_order == 1 and plan.row_blocks > 1
+    assert plan.block_order == order and plan.row_blocks > 1
+    w = (plan.row_blocks + 1) // 2 if order == 2 else plan.row_blocks
     seen = {}
     for L in range(plan.grid_x):
-        d = _decode_block(L, plan.row_blocks, plan.num_chunk_ids, p.num_kv_heads)
+        d = _decode_block(L, plan.row_blocks, plan.num_chunk_ids, p.num_kv_heads, order)
         if d is None:
             continue
-        assert d not in seen
-        seen[d] = L
+        if order == 2:
+            # The pair's blocks add up to RB - 1: every workgroup gets an equal
+            # share of a causal group's work.
+            assert len(d) == 1 or d[0][2] + d[1][2] == plan.row_blocks - 1
+        for t in d:
+            assert t not in seen
+            seen[t] = L
     assert len(seen) == plan.num_chunk_ids * p.num_kv_heads * plan.row_blocks
     per_xcd = [0] * 8
     for item in range(plan.num_chunk_ids):
         for h in range(p.num_kv_heads):
             Ls = [seen[(item, h, rb)] for rb in range(plan.row_blocks)]
             assert len({L % 8 for L in Ls}) == 1
-            assert max(Ls) // (8 * plan.row_blocks) == min(Ls) // (8 * plan.row_blocks)
+            assert max(Ls) // (8 * w) == min(Ls) // (8 * w)
             assert seen[(item, h, plan.row_blocks - 1)] == min(Ls)
             per_xcd[Ls[0] % 8] += 1
     assert max(per_xcd) - min(per_xcd) <= 1

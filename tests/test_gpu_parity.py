@@ -228,6 +228,36 @@ def test_long_request_moves_the_page_window(gpu_lib):
         compare(p, *to_f64(out, lse), *oracle_of(p), what="long request")
 
 
+# ---------------------------------------------------------------- paired row blocks
+
+# Plans with many row blocks per CU pair them: one workgroup runs blocks
+# RB - 1 - k and k of its (item, KV head) as two segments of one ring. A small
+# planned CU count forces that here. Shorter requests have fewer blocks, so the
+# longer block of a pair can be empty while the shorter one is not.
+PAIR_CASES = {
+    "causal_mixed_L": dict(prefix_lens=[0, 35, 200], qo_lens=[300, 129, 40], num_qo_heads=16,
+                           num_kv_heads=2, head_dim=128),
+    "fp8": dict(prefix_lens=[64, 0], qo_lens=[90, 200], num_qo_heads=16, num_kv_heads=2,
+                head_dim=128, kv_dtype="e4m3", fp8_absmax_scales=True),
+    "d64": dict(prefix_lens=[10, 300], qo_lens=[150, 70], num_qo_heads=24, num_kv_heads=3,
+                head_dim=64),
+    "tree_mask": dict(prefix_lens=[500, 100], qo_lens=[48, 33], num_qo_heads=64, num_kv_heads=8,
+                      head_dim=128, mask_kind="tree"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PAIR_CASES))
+@pytest.mark.parametrize("chunk", [-1, 64])
+def test_paired_row_blocks_match_oracle(gpu_lib, name, chunk):
+    p = make_case(94, **PAIR_CASES[name])
+    plan = gpu_lib.vat_plan(_problem(gpu_lib, p, num_cus=4, chunk_keys=chunk))
+    say(f"[paired blocks {name} chunk={chunk}] row_blocks={plan.row_blocks} "
+        f"block_order={plan.block_order} direct={plan.direct} grid={plan.grid_x}")
+    assert plan.block_order == 2 and plan.row_blocks > 1
+    out, lse = run_gpu(gpu_lib, p, num_cus=4, chunk_keys=chunk)
+    compare(p, *to_f64(out, lse), *oracle_of(p), what=f"paired {name} chunk {chunk}")
+
+
 # ---------------------------------------------------------------- graph capture
 
 
