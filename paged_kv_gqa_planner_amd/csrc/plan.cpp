@@ -188,7 +188,8 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   // with one item writes its output directly, the others go through the
   // log-sum-exp merge. The planner sizes C from the page-table capacity so
   // that the items about fill the compute units once (the streaming kernel
-  // holds one workgroup per CU), within [kMinChunkKeys, kMaxChunkKeys]; a
+  // holds one workgroup per CU), at least kMinChunkKeys (the row-tiled
+  // kernel's also at most kMaxChunkKeys); a
   // row-tiled plan whose (request, KV head, row block) items already cover
   // the chip four times over is not split at all.
   const int64_t total_keys = int64_t(p->num_kv_indices) * p->page_size;
@@ -205,13 +206,15 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   } else if (stream) {
     // Split the average request evenly into as many chunks as leave one
     // workgroup per CU: with equal request lengths every chunk then has the
-    // same length and the items fill the CUs exactly once.
+    // same length and the items fill the CUs exactly once. No upper bound:
+    // capping the length would leave a short remainder chunk per request,
+    // whose workgroups take CUs in the first round and push full-length ones
+    // into a second (a long chunk only moves the page window).
     const int64_t per_req = cdiv(total_keys, p->batch);
     int64_t nchunk = int64_t(num_cus) / (int64_t(p->batch) * p->num_kv_heads * RB);
     if (nchunk < 1) nchunk = 1;
     ck = cdiv(cdiv(per_req, nchunk), kChunkQuantum) * kChunkQuantum;
     if (ck < kMinChunkKeys) ck = kMinChunkKeys;
-    if (ck > kMaxChunkKeys) ck = kMaxChunkKeys;
   } else {
     ck = cdiv(total_keys * p->num_kv_heads * RB, 4 * int64_t(num_cus));
     ck = cdiv(ck, kChunkQuantum) * kChunkQuantum;

@@ -32,8 +32,8 @@ constexpr int kStreamPageWindow = 2048;
 constexpr int kMergeRows = 4;
 constexpr int kMergeRows4 = 16;
 constexpr int kMergeThreads = 256;
-// Chunk lengths the planner picks are multiples of kChunkQuantum within
-// [kMinChunkKeys, kMaxChunkKeys].
+// Chunk lengths the planner picks are multiples of kChunkQuantum, at least
+// kMinChunkKeys (and for the row-tiled kernel at most kMaxChunkKeys).
 constexpr int kChunkQuantum = 16;
 constexpr int kMinChunkKeys = 128;
 constexpr int kMaxChunkKeys = 2048;
