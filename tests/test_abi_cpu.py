@@ -203,6 +203,30 @@ def test_row_blocks_of_a_group_share_an_xcd(lib, cid, order):
     assert max(per_xcd) - min(per_xcd) <= 1
 
 
+@pytest.mark.parametrize("batch,Hkv,G,L,prefix", [(4, 8, 8, 64, 8192), (2, 8, 8, 40, 30000),
+                                                   (8, 4, 8, 48, 5000), (3, 8, 16, 20, 12345)])
+def test_equal_requests_split_into_equal_cu_filling_chunks(lib, batch, Hkv, G, L, prefix):
+    """Streaming chunk plans cut the average request into floor(CUs / (B Hkv RB))
+    chunks of equal length (no remainder chunk), so equal requests fill the
+    CUs at most once: a short remainder chunk would take a CU in the first
+    round and push a full-length chunk into a second."""
+    kv_len = prefix + L
+    pages = -(-kv_len // 16)
+    prob = B.make_problem(
+        batch=batch, num_qo_heads=G * Hkv, num_kv_heads=Hkv, head_dim=128, page_size=16,
+        num_pages=batch * pages, num_kv_indices=batch * pages, num_qo_tokens=batch * L,
+        max_qo_len=L, q_dtype=1, kv_dtype=1, has_mask=0, num_cus=256)
+    plan = B.vat_plan(prob)
+    assert plan.kernel == 1 and plan.slices == 0 and plan.row_blocks > 1
+    RB = plan.row_blocks
+    want = max(1, 256 // (batch * Hkv * RB))
+    chunks = -(-kv_len // plan.chunk_keys)
+    assert chunks == want
+    # The last chunk is not a short remainder: it holds more than half a chunk.
+    assert kv_len - (chunks - 1) * plan.chunk_keys > plan.chunk_keys // 2
+    assert batch * Hkv * RB * chunks <= 256
+
+
 def test_chunk_ids_of_consecutive_requests_are_disjoint():
     # Host-side check of the id layout the kernels use: request b's chunks are
     # start_b .. start_b + ceil(kv_len_b / C) - 1 with
