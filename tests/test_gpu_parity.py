@@ -157,6 +157,39 @@ def test_page_permutation_is_bitwise_invariant(gpu_lib):
     assert torch.equal(lse0, lse1)
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "e4m3", "f32"])
+def test_pages_past_4_gib_of_the_pool_are_addressed_exactly(gpu_lib, kv_dtype):
+    """The same pages placed beyond byte offset 4.5 GiB of a larger pool (in
+    reverse order) give bitwise the same result: page bases are 64-bit."""
+    q_dtype = "f32" if kv_dtype == "f32" else "bf16"
+    kw = dict(prefix_lens=[700, 90, 1500], qo_lens=[5, 2, 9], num_qo_heads=32, num_kv_heads=8,
+              head_dim=128, q_dtype=q_dtype, kv_dtype=kv_dtype, mask_kind="tree")
+    base = make_case(57, **kw)
+    t = to_device(base)
+    out0, lse0 = run_gpu(gpu_lib, base, tensors=t)
+    out0, lse0 = out0.clone(), lse0.clone()
+    page_bytes = t["k_cache"][0].numel() * t["k_cache"].element_size()
+    high = -(-(9 << 29) // page_bytes)  # first slot at or past 4.5 GiB
+    n = base.num_pages
+    say(f"pool of {high + n} pages of {page_bytes} B ({kv_dtype})")
+    dst = high + torch.arange(n - 1, -1, -1, device="cuda")
+    big = {}
+    for name in ("k_cache", "v_cache"):
+        src = t[name].view(torch.uint8)
+        pool = torch.empty((high + n,) + tuple(src.shape[1:]), dtype=torch.uint8, device="cuda")
+        pool[dst] = src
+        big[name] = pool.view(t[name].dtype)
+    t2 = dict(t, k_cache=big["k_cache"], v_cache=big["v_cache"],
+              kv_indices=dst[t["kv_indices"].long()].to(torch.int32))
+    out1, lse1 = run_gpu(gpu_lib, base, tensors=t2)
+    same = torch.equal(out0.view(torch.int16), out1.view(torch.int16)) if out0.dtype == torch.bfloat16 \
+        else torch.equal(out0.view(torch.int32), out1.view(torch.int32))
+    assert same
+    assert torch.equal(lse0, lse1)
+    del big, t2, out1, lse1
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("chunk", [-1, 0])
 def test_chain_mask_bitwise_equals_causal(gpu_lib, chunk):
     kw = dict(prefix_lens=[100, 3, 640], qo_lens=[6, 4, 17], num_qo_heads=8, num_kv_heads=2,
