@@ -191,6 +191,41 @@ def test_no_drafts_changes_nothing(gpu_lib):
     _check(gpu_lib, p, k_new, k_new.copy(), "bf16", 1.0, 1.0, "no drafts")
 
 
+@pytest.mark.parametrize("cache_dtype", ["bf16", "e4m3", "f32"])
+def test_writes_past_4_gib_of_the_pool_land_exactly(gpu_lib, cache_dtype):
+    """The same pages placed beyond byte offset 4.5 GiB of a larger pool (in
+    reverse order) receive bitwise the same drafts, and the poisoned slots
+    below them stay untouched: slot addresses are 64-bit."""
+    src = "f32" if cache_dtype == "f32" else "bf16"
+    p = make_case(58, prefix_lens=[300, 40, 900], qo_lens=[5, 3, 8], num_qo_heads=32,
+                  num_kv_heads=8, head_dim=128, q_dtype=src, kv_dtype=cache_dtype, name="big pool")
+    k_new, v_new = make_append_inputs(p, src, seed=11, spread=1.0)
+    fresh = to_device(p)
+    t = _run(gpu_lib, p, k_new, v_new, src, p.k_scale, p.v_scale)
+    page_bytes = fresh["k_cache"][0].numel() * fresh["k_cache"].element_size()
+    high = -(-(9 << 29) // page_bytes)  # first slot at or past 4.5 GiB
+    n = p.num_pages
+    say(f"[append big pool] {high + n} pages of {page_bytes} B, cache={cache_dtype}")
+    dst = high + torch.arange(n - 1, -1, -1, device="cuda")
+    poison = 0x5A
+    big = dict(fresh)
+    pools = {}
+    for name in ("k_cache", "v_cache"):
+        raw = fresh[name].view(torch.uint8)
+        pool = torch.full((high + n,) + tuple(raw.shape[1:]), poison, dtype=torch.uint8, device="cuda")
+        pool[dst] = raw
+        pools[name] = pool
+        big[name] = pool.view(fresh[name].dtype)
+    big["kv_indices"] = dst[fresh["kv_indices"].long()].to(torch.int32)
+    _run(gpu_lib, p, k_new, v_new, src, p.k_scale, p.v_scale, tensors=big)
+    for name in ("k_cache", "v_cache"):
+        pool = pools[name]
+        assert torch.equal(pool[dst], t[name].view(torch.uint8)), name
+        assert not bool((pool[:high] != poison).any()), name
+    del big, pools, pool
+    torch.cuda.empty_cache()
+
+
 def test_repeat_writes_are_identical(gpu_lib):
     p = make_config(5)
     k_new, v_new = make_append_inputs(p, "bf16", seed=10, spread=2.0)
