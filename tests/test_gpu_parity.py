@@ -103,6 +103,21 @@ def test_edge_cases(gpu_lib, name, chunk):
     compare(p, *to_f64(out, lse), *oracle_of(p), what=name)
 
 
+@pytest.mark.parametrize("kv_dtype,head_dim", [("f32", 64), ("bf16", 128), ("bf16", 64),
+                                               ("e4m3", 128), ("e4m3", 64)])
+@pytest.mark.parametrize("mask_kind", ["tree", "random"])
+@pytest.mark.parametrize("chunk", [-1, 64])
+def test_masks_at_the_64_draft_maximum(gpu_lib, kv_dtype, head_dim, mask_kind, chunk):
+    q_dtype = "f32" if kv_dtype == "f32" else "bf16"
+    p = make_case(88, prefix_lens=[100, 0, 37], qo_lens=[64, 64, 1], num_qo_heads=8, num_kv_heads=2,
+                  head_dim=head_dim, q_dtype=q_dtype, kv_dtype=kv_dtype, mask_kind=mask_kind,
+                  fp8_absmax_scales=(kv_dtype == "e4m3"), mask_density=0.4)
+    assert p.max_qo_len == 64
+    say(f"[64 drafts] {kv_dtype} D{head_dim} mask={mask_kind} chunk={chunk}")
+    out, lse = run_gpu(gpu_lib, p, chunk_keys=chunk)
+    compare(p, *to_f64(out, lse), *oracle_of(p), what=f"64 drafts {kv_dtype} D{head_dim} {mask_kind}")
+
+
 def test_fully_masked_rows_give_zero_and_minus_inf(gpu_lib):
     p = make_case(5, prefix_lens=[0, 0], qo_lens=[6, 9], num_qo_heads=4, num_kv_heads=1,
                   head_dim=64, page_size=4, q_dtype="f32", kv_dtype="f32", mask_kind="random",
