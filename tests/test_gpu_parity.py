@@ -118,6 +118,19 @@ def test_masks_at_the_64_draft_maximum(gpu_lib, kv_dtype, head_dim, mask_kind, c
     compare(p, *to_f64(out, lse), *oracle_of(p), what=f"64 drafts {kv_dtype} D{head_dim} {mask_kind}")
 
 
+@pytest.mark.parametrize("kv_dtype,head_dim", [("bf16", 128), ("e4m3", 128), ("f32", 64), ("e4m3", 64)])
+@pytest.mark.parametrize("page_size", [2, 8, 32, 128, 256])
+@pytest.mark.parametrize("chunk", [-1, 0])
+def test_every_page_size(gpu_lib, kv_dtype, head_dim, page_size, chunk):
+    q_dtype = "f32" if kv_dtype == "f32" else "bf16"
+    p = make_case(89, prefix_lens=[700, 3, 1300], qo_lens=[6, 2, 9], num_qo_heads=16, num_kv_heads=4,
+                  head_dim=head_dim, page_size=page_size, q_dtype=q_dtype, kv_dtype=kv_dtype,
+                  mask_kind="tree", fp8_absmax_scales=(kv_dtype == "e4m3"))
+    say(f"[page size {page_size}] {kv_dtype} D{head_dim} chunk={chunk}")
+    out, lse = run_gpu(gpu_lib, p, chunk_keys=chunk)
+    compare(p, *to_f64(out, lse), *oracle_of(p), what=f"page size {page_size} {kv_dtype} D{head_dim}")
+
+
 def test_fully_masked_rows_give_zero_and_minus_inf(gpu_lib):
     p = make_case(5, prefix_lens=[0, 0], qo_lens=[6, 9], num_qo_heads=4, num_kv_heads=1,
                   head_dim=64, page_size=4, q_dtype="f32", kv_dtype="f32", mask_kind="random",
