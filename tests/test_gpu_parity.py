@@ -131,6 +131,20 @@ def test_every_page_size(gpu_lib, kv_dtype, head_dim, page_size, chunk):
     compare(p, *to_f64(out, lse), *oracle_of(p), what=f"page size {page_size} {kv_dtype} D{head_dim}")
 
 
+@pytest.mark.parametrize("kv_dtype,head_dim", [("bf16", 128), ("e4m3", 128), ("f32", 64), ("bf16", 64)])
+@pytest.mark.parametrize("group", [2, 3, 5, 16, 64])
+@pytest.mark.parametrize("mask_kind", ["causal", "tree"])
+def test_query_head_groups(gpu_lib, kv_dtype, head_dim, group, mask_kind):
+    q_dtype = "f32" if kv_dtype == "f32" else "bf16"
+    hkv = 1 if group == 64 else 2
+    p = make_case(90, prefix_lens=[260, 0, 900], qo_lens=[5, 1, 12], num_qo_heads=group * hkv,
+                  num_kv_heads=hkv, head_dim=head_dim, q_dtype=q_dtype, kv_dtype=kv_dtype,
+                  mask_kind=mask_kind, fp8_absmax_scales=(kv_dtype == "e4m3"))
+    say(f"[group {group}] Hkv={hkv} {kv_dtype} D{head_dim} mask={mask_kind}")
+    out, lse = run_gpu(gpu_lib, p)
+    compare(p, *to_f64(out, lse), *oracle_of(p), what=f"group {group} {kv_dtype} D{head_dim} {mask_kind}")
+
+
 def test_fully_masked_rows_give_zero_and_minus_inf(gpu_lib):
     p = make_case(5, prefix_lens=[0, 0], qo_lens=[6, 9], num_qo_heads=4, num_kv_heads=1,
                   head_dim=64, page_size=4, q_dtype="f32", kv_dtype="f32", mask_kind="random",
