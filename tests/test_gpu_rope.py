@@ -73,6 +73,21 @@ def test_query_rope_fuzz(gpu_lib, seed):
     compare(p, *to_f64(*got), *_oracle(p, cs), what=f"rope fuzz {seed}")
 
 
+@pytest.mark.parametrize("kv_dtype,head_dim", [("bf16", 128), ("bf16", 64), ("e4m3", 128)])
+@pytest.mark.parametrize("group,page_size,max_len", [(3, 4, 64), (16, 256, 9), (5, 64, 33)])
+def test_query_rope_groups_page_sizes_and_long_drafts(gpu_lib, kv_dtype, head_dim, group, page_size,
+                                                      max_len):
+    p = make_case(91, prefix_lens=[300, 0, 1100], qo_lens=[max_len, 1, max(1, max_len // 2)],
+                  num_qo_heads=2 * group, num_kv_heads=2, head_dim=head_dim, page_size=page_size,
+                  q_dtype="bf16", kv_dtype=kv_dtype, mask_kind="tree",
+                  fp8_absmax_scales=(kv_dtype == "e4m3"))
+    cs = rope_cos_sin(rope_positions(p) + 1234, head_dim, theta=10000.0)
+    say(f"[rope] {kv_dtype} D{head_dim} G={group} page {page_size} L<={max_len}")
+    got = _rope_run(gpu_lib, p, cs)
+    compare(p, *to_f64(*got), *_oracle(p, cs),
+            what=f"rope {kv_dtype} D{head_dim} G{group} page {page_size}")
+
+
 def test_identity_rotation_equals_the_plain_call_bitwise(gpu_lib):
     p = make_config(3)
     cs = np.concatenate([np.ones((p.num_tokens, 64)), np.zeros((p.num_tokens, 64))],
