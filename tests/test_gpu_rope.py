@@ -147,6 +147,33 @@ def test_cache_write_with_rope_is_bit_exact(gpu_lib, cache_dtype, src, scales, s
                                f"got {got.reshape(-1)[bad[0]]:#x} want {want.reshape(-1)[bad[0]]:#x}")
 
 
+@pytest.mark.parametrize("cache_dtype,src", [("bf16", "bf16"), ("e4m3", "bf16"), ("f32", "f32")])
+@pytest.mark.parametrize("page_size", [1, 4, 64, 256])
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_cache_write_with_rope_at_every_page_size(gpu_lib, cache_dtype, src, page_size, head_dim):
+    p = make_case(43, prefix_lens=[13, 0, 300, 7], qo_lens=[5, 3, 17, 9], num_qo_heads=8,
+                  num_kv_heads=4, head_dim=head_dim, page_size=page_size,
+                  q_dtype="f32" if cache_dtype == "f32" else "bf16", kv_dtype=cache_dtype,
+                  mask_kind="tree")
+    k_new, v_new = make_append_inputs(p, src, seed=8, spread=2.0)
+    cs = rope_cos_sin(rope_positions(p) + 777, head_dim)
+    ks, vs = (0.37, 1.5) if cache_dtype == "e4m3" else (1.0, 1.0)
+    say(f"[rope write {cache_dtype} <- {src} page {page_size} D{head_dim}]")
+    t = to_device(p)
+    gpu_lib.append_kv(_src(k_new, src), _src(v_new, src), t["k_cache"], t["v_cache"],
+                      t["kv_indptr"], t["kv_indices"], t["last_page_len"], t["qo_indptr"],
+                      k_scale=ks, v_scale=vs, k_cos_sin=torch.from_numpy(cs).cuda())
+    torch.cuda.synchronize()
+    want_k, want_v = oracle_append(k_new, v_new, src, p.k_cache, p.v_cache, cache_dtype,
+                                   p.kv_indptr, p.kv_indices, p.last_page_len, p.qo_indptr,
+                                   p.page_size, ks, vs, k_cos_sin=cs)
+    for name, got, want in (("k", _raw(t["k_cache"]), want_k), ("v", _raw(t["v_cache"]), want_v)):
+        want = want.view(np.uint32) if want.dtype == np.float32 else want
+        bad = np.nonzero(got.reshape(-1) != want.reshape(-1))[0]
+        assert bad.size == 0, (f"{name}: {bad.size} words differ; first flat {int(bad[0])}: "
+                               f"got {got.reshape(-1)[bad[0]]:#x} want {want.reshape(-1)[bad[0]]:#x}")
+
+
 @pytest.mark.parametrize("cid", [3, 5])
 def test_write_then_attend_with_rope(gpu_lib, cid):
     """Keys rotated at the cache write, queries in the kernel, same positions:
