@@ -84,3 +84,40 @@ def test_full_rows_under_balanced_slices(gpu_lib, num_cus):
     say(f"[rows slices num_cus={num_cus}]")
     got = run_gpu(gpu_lib, p, num_cus=num_cus)
     compare(p, *to_f64(*got), *oracle_of(p), what=f"rows slices {num_cus}")
+
+
+@pytest.mark.parametrize("kv_dtype,head_dim", [("f32", 64), ("bf16", 128), ("e4m3", 128), ("e4m3", 64)])
+@pytest.mark.parametrize("group,page_size", [(3, 64), (16, 256), (64, 2)])
+def test_full_rows_with_uncommon_groups_and_page_sizes(gpu_lib, kv_dtype, head_dim, group, page_size):
+    hkv = 1 if group == 64 else 2
+    kw = dict(prefix_lens=[120, 0, 700], qo_lens=[40, 1, 64], num_qo_heads=group * hkv,
+              num_kv_heads=hkv, head_dim=head_dim, page_size=page_size,
+              q_dtype="f32" if kv_dtype == "f32" else "bf16", kv_dtype=kv_dtype, mask_kind="tree",
+              fp8_absmax_scales=(kv_dtype == "e4m3"))
+    rows = make_case(92, mask_layout="rows", rows_prefix_fill="random", rows_true_values="random", **kw)
+    bits = make_case(92, **kw)
+    plans = [_plan_of(gpu_lib, x, layout) for x, layout in ((rows, 2), (bits, 1))]
+    say(f"[rows G={group} page {page_size}] {kv_dtype} D{head_dim} same plan: {plans[0] == plans[1]}")
+    got_rows = run_gpu(gpu_lib, rows)
+    compare(rows, *to_f64(*got_rows), *oracle_of(rows), what=f"rows G{group} page {page_size}")
+    got_bits = run_gpu(gpu_lib, bits)
+    compare(bits, *to_f64(*got_bits), *oracle_of(bits), what=f"bits G{group} page {page_size}")
+    # A different split or tiling changes only the rounding order, so the two
+    # layouts agree bit for bit exactly when they get the same plan (bf16 D 128
+    # has no two-tile variant for full-row masks).
+    if plans[0] == plans[1]:
+        assert _bitwise_same(got_rows, got_bits), "full-row and packed layouts differ"
+
+
+def _plan_of(lib, p, has_mask):
+    prob = lib.make_problem(
+        batch=p.batch, num_qo_heads=p.num_qo_heads, num_kv_heads=p.num_kv_heads,
+        head_dim=p.head_dim, page_size=p.page_size, num_pages=p.num_pages,
+        num_kv_indices=len(p.kv_indices), num_qo_tokens=int(p.qo_indptr[-1]),
+        max_qo_len=p.max_qo_len, q_dtype={"f32": 0, "bf16": 1}[p.q_dtype],
+        kv_dtype={"f32": 0, "bf16": 1, "e4m3": 2}[p.kv_dtype], has_mask=has_mask,
+        num_mask_bytes=len(p.mask), num_cus=256)
+    d = lib.vat_plan(prob).as_dict()
+    d.pop("lds_bytes", None)
+    d.pop("workspace_bytes", None)
+    return d
