@@ -204,6 +204,9 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
                                               float c, int lane, int kt0) {
   using G = StreamGeom<KV, D, kSWaves, SK>;
   static_assert(KT == 2 || KT == 4 || KT == 8, "one to four 32-key blocks");
+  // Two row tiles per wave: the scheduler interleaves the stage's LDS reads
+  // with its MFMAs (one-tile variants run faster with the default schedule).
+  if constexpr (RT == 2) __builtin_amdgcn_iglp_opt(0);
   constexpr int NDT = D / 16;
   const int l16 = lane & 15;
   const int j4 = lane >> 4;
