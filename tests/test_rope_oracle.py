@@ -73,6 +73,40 @@ def test_binary32_form_equals_torch_float32_arithmetic():
     assert np.array_equal(rope_rotate_f32(x, cs).view(np.uint32), want.view(np.uint32))
 
 
+def _f32_bits(*vals):
+    return np.array(vals, dtype=np.uint32)
+
+
+def test_binary32_invalid_results_are_the_canonical_positive_quiet_nan():
+    # D = 4: pairs (0, 2) and (1, 3). Worked by hand from the rotation
+    # x'_i = x_i c - x_{i+2} s, x'_{i+2} = x_{i+2} c + x_i s, every product
+    # and sum rounded on its own. An invalid operation (inf * 0, inf - inf)
+    # or a NaN operand gives NaN, stored as 0x7FC00000 whatever sign or
+    # payload the hardware would carry; finite and infinite lanes keep
+    # their exact values.
+    inf = np.float32(np.inf)
+    nan_neg = _f32_bits(0xFFC00000).view(np.float32)[0]      # negative quiet NaN
+    nan_sig = _f32_bits(0x7F800001).view(np.float32)[0]      # signalling NaN, payload 1
+    nan_pay = _f32_bits(0xFFC12345).view(np.float32)[0]      # negative NaN with a payload
+    qnan = 0x7FC00000
+    cases = [
+        # pair 0 at a quarter turn (c 0, s 1): inf*0 - 0*1 is NaN, 0*0 + inf*1 = inf;
+        # pair 1 at angle zero (c 1, s 0): 1*1 - 2*0 = 1, 2*1 + 1*0 = 2.
+        ([inf, 1.0, 0.0, 2.0], [0.0, 1.0, 1.0, 0.0], [qnan, 0x3F800000, 0x7F800000, 0x40000000]),
+        # pair 0 at c = s = 1: inf*1 - inf*1 = inf - inf is NaN (x86 makes it
+        # the negative "indefinite" NaN); inf*1 + inf*1 = inf. Pair 1: c 1, s 0.
+        ([inf, 3.0, inf, -1.0], [1.0, 1.0, 1.0, 0.0], [qnan, 0x40400000, 0x7F800000, 0xBF800000]),
+        # NaN operands of either sign and any payload; pair 1's -0 * 1 - 0 * 0 = -0 - 0 = -0.
+        ([nan_neg, -0.0, 1.0, 0.0], [1.0, 1.0, 0.0, 0.0], [qnan, 0x80000000, qnan, 0x00000000]),
+        # pair 0 at c = s = 1/2: 1*0.5 - 2*0.5 = -0.5, 2*0.5 + 1*0.5 = 1.5.
+        ([1.0, nan_sig, 2.0, nan_pay], [0.5, 1.0, 0.5, 0.0], [0xBF000000, qnan, 0x3FC00000, qnan]),
+    ]
+    for x, cs, want in cases:
+        got = rope_rotate_f32(np.array(x, dtype=np.float32), np.array(cs, dtype=np.float32))
+        assert got.dtype == np.float32
+        assert got.view(np.uint32).tolist() == want, (x, cs, [hex(v) for v in got.view(np.uint32)])
+
+
 def test_cos_sin_rows_follow_the_closed_form():
     pos = np.array([0, 1, 17, 4096, 65535])
     np.testing.assert_allclose(rope_cos_sin(pos, 128), closed_form_rows(pos, 128), atol=1e-7)
