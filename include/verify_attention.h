@@ -168,11 +168,22 @@ typedef struct {
 } vat_plan_t;
 
 /* Plan a call: validates the shapes and fills *plan. Host only; touches the
- * GPU only to read the compute-unit count when problem->num_cus == 0. */
+ * GPU only to read the compute-unit count when problem->num_cus == 0.
+ * Planning is separate from running, as in the FlashInfer page "feat:
+ * Separate Q and KV dtypes for decode" (begin_forward docstring: a planning
+ * call builds the auxiliary structures before the forward calls reuse them),
+ * but here the plan depends on shapes alone -- never on device contents -- so
+ * verify_attention replans on every call for free and stays capturable.
+ * Errors: VAT_ERR_NULL for a NULL argument, otherwise those of
+ * verify_attention's host checks; *plan is then unspecified. */
 vat_status_t vat_plan(const vat_problem_t* problem, vat_plan_t* plan);
 
 /* Workspace bytes verify_attention needs for this problem (host only; see
- * vat_plan for the device query). */
+ * vat_plan for the device query). The workspace is the caller-owned scratch
+ * buffer that the same FlashInfer page's begin_forward takes as its first
+ * argument; here it holds the per-split partial outputs and log-sum-exps
+ * (and nothing that must survive between calls). 0 for a direct plan.
+ * Errors: as vat_plan; *bytes is then unchanged. */
 vat_status_t vat_workspace_size(const vat_problem_t* problem, size_t* bytes);
 
 /* The whole path: partial kernel, then (unless the plan is direct) the
@@ -284,6 +295,17 @@ vat_status_t vat_append_kv_rope(const vat_problem_t* problem, int32_t src_dtype,
                                 const int32_t* kv_indices, const int32_t* last_page_len,
                                 const int32_t* qo_indptr, const float* k_cos_sin, float k_scale,
                                 float v_scale, void* stream);
+
+/* Measurement aid, not a step of the path: read `bytes` of device memory at
+ * `buf` once, start to end, with 16-byte non-temporal loads spread over
+ * every compute unit (eight workgroups per CU), and enqueue nothing else.
+ * The time it takes gives the HBM read rate reachable with the plainest
+ * access pattern, reported beside the chip's published peak when the
+ * attention kernels' bandwidth is judged. buf: 16-byte aligned, bytes a
+ * multiple of 16 (VAT_ERR_ALIGN / VAT_ERR_SHAPE otherwise); sink: one
+ * device uint32 that the kernel almost never writes (it exists so that the
+ * loads cannot be optimised away). bytes == 0 enqueues nothing. */
+vat_status_t vat_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 /* Static description of a status code. */
 const char* vat_status_string(vat_status_t status);

@@ -89,6 +89,8 @@ def load(path: Optional[str] = None):
     lib.vat_append_kv.argtypes = [P(VatProblem), ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp,
                                   f, f, vp]
     lib.vat_append_kv.restype = ctypes.c_int
+    lib.vat_read_probe.argtypes = [vp, ctypes.c_size_t, vp, vp]
+    lib.vat_read_probe.restype = ctypes.c_int
     lib.vat_status_string.argtypes = [ctypes.c_int]
     lib.vat_status_string.restype = ctypes.c_char_p
     lib.vat_abi_version.argtypes = []
@@ -144,9 +146,15 @@ def problem_from_tensors(q, k_cache, kv_indptr, kv_indices, mask=None, max_qo_le
     batch = kv_indptr.numel() - 1
     T = q.shape[0]
     if max_qo_len is None:
-        # Shape-only bound: one request may hold every token but the others' one.
-        max_qo_len = T - max(batch - 1, 0) if batch > 0 else 0
-        max_qo_len = max(max_qo_len, 0)
+        # One request holds every query row. With more requests the bound
+        # cannot come from shapes alone without overstating it (T - (B - 1)
+        # may pass the 64-draft mask limit, and a loose bound inflates the
+        # planned rows per KV head), and reading qo_indptr would synchronise:
+        # the caller states it.
+        if batch > 1 and T > 0:
+            raise ValueError("max_qo_len is required when the batch holds more than one "
+                             "request (the largest qo_indptr[b+1] - qo_indptr[b])")
+        max_qo_len = T if batch > 0 else 0
     return make_problem(
         batch=batch, num_qo_heads=q.shape[1], num_kv_heads=k_cache.shape[2], head_dim=q.shape[2],
         page_size=k_cache.shape[1], num_pages=k_cache.shape[0], num_kv_indices=kv_indices.numel(),
@@ -236,8 +244,9 @@ def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, 
                      q_cos_sin=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """Multi-query verification attention over a paged KV cache; returns (out, lse).
 
-    ``sm_scale`` defaults to ``head_dim ** -0.5``; ``max_qo_len`` defaults to
-    the shape-only bound ``T - (B - 1)``; ``chunk_keys`` -1 lets the planner
+    ``sm_scale`` defaults to ``head_dim ** -0.5``; ``max_qo_len`` (the largest
+    request's query-token count) may be omitted only for a batch of one
+    request, where it is T, or when there are no query tokens; ``chunk_keys`` -1 lets the planner
     choose the prefix split, 0 forces one work item per request (direct
     output), a positive multiple of 16 forces that chunk length.
     ``mask_layout``: "bits" (packed L x L blocks) or "rows" (sglang's full
@@ -248,12 +257,14 @@ def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, 
     problem, sm, out, lse, workspace, ws_bytes = _prepare(
         q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr, mask, mask_indptr,
         sm_scale, max_qo_len, out, lse, workspace, chunk_keys, num_cus, mask_layout, q_cos_sin)
-    st = lib.verify_attention_rope(ctypes.byref(problem), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                   _ptr(kv_indptr), _ptr(kv_indices), _ptr(last_page_len),
-                                   _ptr(qo_indptr), _ptr(mask), _ptr(mask_indptr),
-                                   _ptr(q_cos_sin), sm, float(k_scale), float(v_scale), _ptr(out),
-                                   _ptr(lse), _ptr(workspace), ws_bytes, _stream_handle(stream))
-    _check(st, "verify_attention")
+    head = (ctypes.byref(problem), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_indptr),
+            _ptr(kv_indices), _ptr(last_page_len), _ptr(qo_indptr), _ptr(mask), _ptr(mask_indptr))
+    tail = (sm, float(k_scale), float(v_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+            _stream_handle(stream))
+    if q_cos_sin is None:
+        _check(lib.verify_attention(*head, *tail), "verify_attention")
+    else:
+        _check(lib.verify_attention_rope(*head, _ptr(q_cos_sin), *tail), "verify_attention_rope")
     return out, lse
 
 
@@ -379,6 +390,15 @@ class PreparedCall:
             _check(self.lib.verify_attention(*self.args), "verify_attention")
         return self.out, self.lse
 
+    def call_on(self, stream):
+        """The whole call enqueued on ``stream`` (e.g. a graph-capture stream)."""
+        h = _stream_handle(stream)
+        if self.rope:
+            _check(self.lib.verify_attention_rope(*self.rope_args[:-1], h), "verify_attention_rope")
+        else:
+            _check(self.lib.verify_attention(*self.args[:-1], h), "verify_attention")
+        return self.out, self.lse
+
     def partial(self):
         if self.rope:
             _check(self.lib.vat_launch_partial_rope(*self.rope_args), "vat_launch_partial_rope")
@@ -387,3 +407,12 @@ class PreparedCall:
 
     def merge(self):
         _check(self.lib.vat_launch_merge(*self.merge_args), "vat_launch_merge")
+
+
+def read_probe(buf, sink, stream=None):
+    """Enqueue one streaming read of the whole device tensor ``buf`` (a
+    measurement aid: the plainest HBM read, for the roofline); ``sink`` is a
+    one-element int32 device tensor."""
+    lib = load()
+    n = buf.numel() * buf.element_size()
+    _check(lib.vat_read_probe(_ptr(buf), n, _ptr(sink), _stream_handle(stream)), "vat_read_probe")

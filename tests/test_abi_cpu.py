@@ -481,3 +481,35 @@ int main() {
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "planned" in r.stdout
+
+
+def test_binding_requires_max_qo_len_for_batches_of_several_requests():
+    """The binding's only shape-derived bound is for one request (L = T); a
+    batch of several must state the largest draft count, since T - (B - 1)
+    would overstate it (and pass the 64-draft mask limit)."""
+    import torch
+
+    q = torch.zeros(136, 4, 128, dtype=torch.bfloat16)
+    kc = torch.zeros(40, 16, 1, 128, dtype=torch.bfloat16)
+    one = torch.tensor([0, 3], dtype=torch.int32)
+    eight = torch.arange(0, 9 * 3, 3, dtype=torch.int32)
+    idx = torch.arange(40, dtype=torch.int32)
+    assert B.problem_from_tensors(q, kc, one, idx).max_qo_len == 136
+    assert B.problem_from_tensors(q[:0], kc, torch.zeros(1, dtype=torch.int32), idx).max_qo_len == 0
+    assert B.problem_from_tensors(q[:0], kc, eight, idx).max_qo_len == 0  # no tokens at all
+    with pytest.raises(ValueError, match="max_qo_len"):
+        B.problem_from_tensors(q, kc, eight, idx)
+    with pytest.raises(ValueError, match="max_qo_len"):
+        B.problem_from_tensors(q, kc, eight, idx, mask=torch.zeros(300, dtype=torch.uint8))
+    assert B.problem_from_tensors(q, kc, eight, idx, max_qo_len=17).max_qo_len == 17
+
+
+def test_read_probe_host_checks(lib):
+    """The HBM read probe rejects bad arguments before touching a device."""
+    vp = ctypes.c_void_p
+    assert lib.vat_read_probe(None, 0, None, None) == 0            # nothing to read
+    assert lib.vat_read_probe(None, 64, vp(4096), None) == 1       # NULL buffer
+    assert lib.vat_read_probe(vp(4096), 64, None, None) == 1       # NULL sink
+    assert lib.vat_read_probe(vp(4096), 72, vp(8192), None) == 2   # not a multiple of 16
+    assert lib.vat_read_probe(vp(4104), 64, vp(8192), None) == 4   # buffer misaligned
+    assert lib.vat_read_probe(vp(4096), 64, vp(8194), None) == 4   # sink misaligned

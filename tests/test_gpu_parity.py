@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests.gpu_helpers import compare, oracle_of, rows_of, run_gpu, say, to_device, to_f64
+from tests.gpu_helpers import compare, oracle_of, run_gpu, say, to_device, to_f64
 from workloads import make_case, make_config
 
 pytestmark = pytest.mark.gpu
@@ -25,18 +25,35 @@ CONFIG_CASES = [(1, None), (2, None), (3, 4096), (3, 16384), (3, 32768), (4, Non
 
 
 @pytest.mark.parametrize("cid,prefix", CONFIG_CASES, ids=lambda x: str(x))
-def test_config_parity(gpu_lib, cid, prefix):
+def test_config_parity(gpu_lib, oracle_pool, cid, prefix):
+    """Every request of every workload against the oracle (spread over host
+    cores by (request, KV head))."""
     p = make_config(cid, prefix=prefix or 4096)
     say(f"[config {cid} prefix={prefix}] {p.name}")
     plan = gpu_lib.vat_plan(_problem(gpu_lib, p)).as_dict()
     say(f"  plan {plan}")
     out, lse = run_gpu(gpu_lib, p)
     got_o, got_l = to_f64(out, lse)
-    requests = {4: [0, 9], 7: [0, 3]}.get(cid)
-    ref_o, ref_l = oracle_of(p, requests=requests)
-    rows = None if requests is None else rows_of(p, requests)
-    eo, el = compare(p, got_o, got_l, ref_o, ref_l, rows=rows, what=f"config {cid}")
-    say(f"  max|out err| {eo:.3e}  max|lse err| {el:.3e}")
+    ref_o, ref_l = oracle_pool.run(p)
+    eo, el = compare(p, got_o, got_l, ref_o, ref_l, what=f"config {cid}")
+    say(f"  max|out err| {eo:.3e}  max|lse err| {el:.3e} ({oracle_pool.workers} oracle workers)")
+
+
+def test_default_max_qo_len_and_sm_scale_for_one_request(gpu_lib):
+    """The binding's defaults: one request's bound is T, sm_scale is D^-0.5."""
+    p = make_config(3, prefix=4096)
+    assert p.batch == 1 and abs(p.sm_scale - p.head_dim ** -0.5) < 1e-7  # float32 rounding
+    t = to_device(p)
+    out, lse = gpu_lib.verify_attention(t["q"], t["k_cache"], t["v_cache"], t["kv_indptr"],
+                                        t["kv_indices"], t["last_page_len"], t["qo_indptr"],
+                                        t["mask"], t["mask_indptr"])
+    torch.cuda.synchronize()
+    compare(p, *to_f64(out, lse), *oracle_of(p), what="defaults")
+    with pytest.raises(ValueError, match="max_qo_len"):
+        q = make_config(2)
+        tq = to_device(q)
+        gpu_lib.verify_attention(tq["q"], tq["k_cache"], tq["v_cache"], tq["kv_indptr"],
+                                 tq["kv_indices"], tq["last_page_len"], tq["qo_indptr"])
 
 
 def _problem(lib, p, **kw):
