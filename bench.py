@@ -1,6 +1,10 @@
 """Throughput of multi-query verification attention over a paged KV cache on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--prefix 4096]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5] [--prefix 4096]
+
+The default workload is config 5 -- bf16 queries over an fp8 e4m3 KV cache,
+batch 64, prefixes U[512, 8192], dynamic draft lengths -- the largest of the
+KV-bound verify workloads; ``--config`` picks any other.
 
 One step is one ``verify_attention`` call -- partial kernel plus log-sum-exp
 merge -- over one batch of seeded synthetic inputs already resident in HBM.
@@ -9,16 +13,27 @@ copies of the page pool (each with its own page table), together larger than
 the 256 MB Infinity Cache, so every step streams its KV cache from HBM.
 
 Before timing, the output of every copy is checked: copy 0 against the CPU
-oracle at the parity tolerances, the others bitwise against copy 0. The
-timed K steps run back to back on one stream; the stream is first held by a
-short GPU sleep so that the host has queued all K steps before the first
-one starts and HIP events measure GPU time only. A second run of K partial
-kernels alone, timed the same way, gives that kernel's average duration,
-from which the roofline fraction is computed with the algorithmic bytes
-(KV-bound workloads) or FLOPs (prefill).
+oracle at the parity tolerances (every request), the others bitwise against
+copy 0. Timings:
 
-Prints one JSON line. The oracle (single-threaded NumPy float64) is timed on
-the host on the same workload as the ``cpu_baseline`` leg.
+* ``ms_per_step`` / ``value``: K steps back to back on one stream, averaged;
+  the stream is first held by a short GPU sleep so that the host has queued
+  all K steps before the first one starts and HIP events measure GPU time
+  only.
+* ``roofline``: K partial kernels alone, timed the same way, give that
+  kernel's average duration, from which the roofline fraction is computed
+  with the algorithmic bytes (KV-bound workloads) or FLOPs (prefill shapes).
+* ``per_call``: one call captured in a HIP graph (one graph per pool copy)
+  and replayed K times with a cache flush (1 GiB written, then read) before
+  each replay: median, p10 and p90 of the per-call GPU times, plus the
+  median of K warm replays without a flush.
+* ``hbm_read_probe``: the library's plain streaming-read kernel over 2 GiB,
+  the HBM read rate reachable on this chip, beside the published peak.
+
+The oracle (NumPy float64) runs on the host's cores, spread over (request,
+KV head) items in worker processes with one BLAS thread each, on the whole
+workload: its wall time is the ``cpu_baseline`` leg, with the worker count
+and CPU model stated.
 
 ``--op append`` times the step before the path instead: ``vat_append_kv``
 writing the workload's draft keys and values (fresh seeded values, bf16, or
@@ -99,28 +114,6 @@ def algorithmic_work(p):
             pairs += L * prefix + bits
     flops = 4 * p.head_dim * p.num_qo_heads * pairs
     return kvb, flops
-
-
-def timed_oracle(p, min_seconds: float, requests=None, q_cos_sin=None):
-    """Oracle wall time on this host with one BLAS thread; repeats the sample
-    until ``min_seconds`` have passed (at least once)."""
-    from threadpoolctl import threadpool_limits
-
-    from oracle import verify_attention as oracle_va
-
-    reps = 0
-    t0 = time.perf_counter()
-    with threadpool_limits(1):
-        while True:
-            ref = oracle_va(p.q, p.k_cache, p.v_cache, p.kv_indptr, p.kv_indices, p.last_page_len,
-                            p.qo_indptr, p.mask, p.mask_indptr, sm_scale=p.sm_scale,
-                            k_scale=p.k_scale, v_scale=p.v_scale, q_dtype=p.q_dtype,
-                            kv_dtype=p.kv_dtype, requests=requests, mask_layout=p.mask_layout,
-                            q_cos_sin=q_cos_sin)
-            reps += 1
-            if time.perf_counter() - t0 >= min_seconds:
-                break
-    return ref, (time.perf_counter() - t0), reps
 
 
 def profiled_traffic(key: str, src_hash: str):
@@ -321,6 +314,89 @@ def bench_append(args, p, dev):
         sys.exit(3)
 
 
+def graph_call_stats(torch, binding, batches, K, flush_bytes):
+    """Per-call GPU times (ms) of one ``verify_attention`` call replayed from a
+    HIP graph: ``flushed`` with a cache flush before every call (a 1 GiB
+    write, then a read of the same buffer, so the 256 MB Infinity Cache and
+    the L2s hold nothing of the call's inputs and nothing dirty), and
+    ``warm`` with the same call replayed back to back. One graph per pool
+    copy; flushed calls rotate over the copies. The stream is held by a GPU
+    sleep while the host queues all calls, so each event pair brackets only
+    the graph's own GPU work."""
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for call in batches:
+            call.call_on(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for call in batches:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call.call_on(torch.cuda.current_stream())
+        graphs.append(g)
+    torch.cuda.synchronize()
+    flush_buf = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def flush(i):
+        flush_buf.fill_(i & 0xFF)
+        binding.read_probe(flush_buf, sink)
+
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    torch.cuda._sleep(1_000_000)
+    c1.record()
+    torch.cuda.synchronize()
+    cycles_per_ms = 1_000_000 / max(c0.elapsed_time(c1), 1e-3)
+
+    def run(with_flush):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)]
+        t_host = time.perf_counter()
+        for i in range(3):
+            if with_flush:
+                flush(i)
+            graphs[i % len(graphs)].replay()
+        host_per = (time.perf_counter() - t_host) / 3
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int((20.0 + 2.0 * K * host_per * 1e3) * cycles_per_ms))
+        for i in range(K):
+            if with_flush:
+                flush(i)
+            ev[i][0].record()
+            graphs[i % len(graphs) if with_flush else 0].replay()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev])
+
+    flushed = run(True)
+    warm = run(False)
+    del graphs
+    return flushed, warm
+
+
+def read_probe_gbps(torch, binding, nbytes, reps=10):
+    """HBM read rate of the library's streaming-read probe over ``nbytes``
+    (GB/s per launch: median and best of ``reps``)."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(3)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        binding.read_probe(buf, sink)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        binding.read_probe(buf, sink)
+        b.record()
+    torch.cuda.synchronize()
+    rates = np.array([nbytes / (a.elapsed_time(b) * 1e-3) / 1e9 for a, b in ev])
+    del buf
+    return float(np.median(rates)), float(rates.max())
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -328,7 +404,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--op", default="verify", choices=["verify", "append"],
                     help="verify: the attention path; append: the draft K/V cache write")
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5, 6, 7],
+                    help="workload (default 5: bf16 Q over an fp8 e4m3 KV cache, batch 64, "
+                         "the largest of the KV-bound verify workloads)")
     ap.add_argument("--prefix", type=int, default=4096, help="prefix length for config 3")
     ap.add_argument("--rope", action="store_true",
                     help="rotate the queries by RoPE at their tree positions inside the kernel "
@@ -342,6 +420,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum host time spent timing the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph-stats", action="store_true",
+                    help="skip the per-call graph-replay timings and the HBM read probe")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run K device-to-device copies of MIB MiB (for scaling HBM "
                          "byte counters) and exit")
@@ -353,6 +433,20 @@ def main():
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
+    # The oracle's worker processes start before this process touches the GPU.
+    pool = None
+    if not args.copy_calibration and args.op == "verify":
+        from tests.oracle_pool import OraclePool
+
+        pool = OraclePool()
+    try:
+        run_bench(args, pool)
+    finally:
+        if pool is not None:
+            pool.close()
+
+
+def run_bench(args, pool):
     import torch
 
     from paged_kv_gqa_planner_amd import binding
@@ -387,7 +481,7 @@ def main():
     pool_bytes = 2 * base["k_cache"].numel() * base["k_cache"].element_size()
     copies = args.copies or max(2, math.ceil((1 << 30) / pool_bytes))
 
-    q_cs = None
+    q_cs = rope_rows = None
     if args.rope:
         from workloads import rope_cos_sin, rope_positions
 
@@ -416,26 +510,18 @@ def main():
         batches.append(call)
     torch.cuda.synchronize()
 
-    # ---- verification: copy 0 against the oracle, the others bitwise against copy 0
-    sample_requests = [0, p.batch - 1] if args.config in (4, 7) else None
-    cpu = None
-    if not args.no_cpu_baseline:
-        ref, cpu_s, cpu_reps = timed_oracle(p, args.cpu_seconds, sample_requests,
-                                            None if q_cs is None else rope_rows)
-        cpu = (cpu_s, cpu_reps)
-    else:
-        ref, _, _ = timed_oracle(p, 0.0, sample_requests, None if q_cs is None else rope_rows)
+    # ---- verification: copy 0 against the oracle (every request), the others
+    # bitwise against copy 0. The oracle's own wall time on the host's cores
+    # is the CPU baseline.
+    ref, cpu_s, cpu_reps = pool.timed(p, 0.0 if args.no_cpu_baseline else args.cpu_seconds,
+                                      q_cos_sin=rope_rows)
     o0, l0 = batches[0]()
     torch.cuda.synchronize()
     o0 = o0.clone()
     l0 = l0.clone()
-    got_o = o0.float().cpu().double().numpy()
-    got_l = l0.cpu().double().numpy()
-    rows = np.arange(tokens)
-    if sample_requests is not None:
-        rows = np.concatenate([np.arange(p.qo_indptr[b], p.qo_indptr[b + 1]) for b in sample_requests])
-    ref_o, ref_l = ref[0][rows], ref[1][rows]
-    go, gl = got_o[rows], got_l[rows]
+    go = o0.float().cpu().double().numpy()
+    gl = l0.cpu().double().numpy()
+    ref_o, ref_l = ref
     ninf_ok = bool(np.array_equal(np.isneginf(ref_l), np.isneginf(gl)))
     fin = ~np.isneginf(ref_l)
     err_o = float(np.abs(go - ref_o).max())
@@ -500,7 +586,8 @@ def main():
     # The bound the workload's arithmetic intensity selects: above the ridge
     # (bf16 MFMA peak / HBM peak, about 312 FLOP per KV byte) the MFMA units
     # bound the kernel (the prefill and the wide trees), below it HBM does.
-    if flops / kvb > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
+    mfma_bound = flops / kvb > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if mfma_bound:
         achieved = flops / (part_avg * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
@@ -541,23 +628,45 @@ def main():
         "partial_kernel_ms": round(part_avg, 5),
         "verified": bool(verified),
         "parity": {"max_out_err": err_o, "max_lse_err": err_l,
-                   "tol_out": TOL_OUT[p.q_dtype], "tol_lse": TOL_LSE,
-                   "sample": "all requests" if sample_requests is None else
-                   f"requests {sample_requests}"},
+                   "tol_out": TOL_OUT[p.q_dtype], "tol_lse": TOL_LSE, "sample": "all requests"},
         "plan": plan,
         "gpu_ran_ahead_of_host": bool(gpu_ran_ahead),
         "kernel_source": src_hash,
     }
-    if cpu is not None:
-        cpu_s, reps = cpu
-        cpu_tokens = tokens if sample_requests is None else int(
-            sum(p.qo_indptr[b + 1] - p.qo_indptr[b] for b in sample_requests))
+    if not args.no_graph_stats:
+        flushed, warm = graph_call_stats(torch, binding, batches, K, 1 << 30)
+        med = float(np.median(flushed))
+        line["per_call"] = {
+            "what": "one verify_attention call replayed from a HIP graph, GPU time by HIP events",
+            "flushed_ms": {"median": round(med, 5),
+                           "p10": round(float(np.percentile(flushed, 10)), 5),
+                           "p90": round(float(np.percentile(flushed, 90)), 5)},
+            "flush": "1 GiB written, then read, between calls",
+            "warm_median_ms": round(float(np.median(warm)), 5),
+            "calls": K,
+            "query_tokens_per_s_flushed_median": round(tokens / (med * 1e-3), 1),
+        }
+        if mfma_bound:
+            line["per_call"]["mfma_frac_flushed_median"] = round(
+                flops / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+        else:
+            line["per_call"]["kv_frac_of_peak_flushed_median"] = round(
+                kvb / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        probe_med, probe_best = read_probe_gbps(torch, binding, 2 << 30)
+        line["hbm_read_probe"] = {"bytes": 2 << 30, "gbps_median": round(probe_med, 1),
+                                  "gbps_best": round(probe_best, 1),
+                                  "frac_of_peak_median": round(probe_med / HBM_PEAK_GBPS, 4),
+                                  "kernel": "vat_read_probe (16-byte non-temporal loads, "
+                                            "8 workgroups per CU)"}
+    if not args.no_cpu_baseline:
+        from tests.oracle_pool import cpu_model
+
         line["cpu_baseline"] = {
-            "value": round(cpu_tokens * reps / cpu_s, 3), "unit": "query-tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": ("whole workload" if sample_requests is None else
-                       f"requests {sample_requests} of the workload") +
-                      f", repeated {reps}x, {cpu_s:.1f} s, NumPy float64 with one BLAS thread"}
+            "value": round(tokens * cpu_reps / cpu_s, 3), "unit": "query-tokens/s",
+            "cores": pool.workers, "kind": "oracle",
+            "sample": f"whole workload, {p.batch * p.num_kv_heads} (request, KV head) items over "
+                      f"{pool.workers} worker processes with one BLAS thread each, repeated "
+                      f"{cpu_reps}x, {cpu_s:.1f} s, NumPy float64; host CPU: {cpu_model()}"}
     print(json.dumps(line), flush=True)
     if not verified:
         sys.exit(3)

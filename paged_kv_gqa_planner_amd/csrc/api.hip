@@ -16,6 +16,7 @@ const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int
 const void* merge_kernel(int q_is_f32, int head_dim, int rows_per_workgroup);
 const void* append_kernel(int src_dtype, int cache_dtype, int pow2_scales, int units);
 const void* append_rope_kernel(int src_dtype, int cache_dtype, int pow2_scales);
+const void* read_probe_kernel();
 }  // namespace vat
 
 namespace {
@@ -382,6 +383,27 @@ vat_status_t vat_append_kv_rope(const vat_problem_t* problem, int32_t src_dtype,
   return append_kv(problem, src_dtype, k_new, v_new, k_cache, v_cache, kv_indptr, kv_indices,
                    last_page_len, qo_indptr, k_cos_sin, true, k_scale, v_scale,
                    (hipStream_t)stream);
+}
+
+vat_status_t vat_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0) return VAT_OK;
+  if (!buf || !sink) return VAT_ERR_NULL;
+  if (bytes % 16 || bytes / 16 > (size_t)INT64_MAX) return VAT_ERR_SHAPE;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return VAT_ERR_ALIGN;
+  int32_t cus = 0;
+  vat_status_t st = device_cus(&cus);
+  if (st != VAT_OK) return st;
+  // Eight workgroups of four waves per CU; each lane keeps four 16-byte loads
+  // in flight per round.
+  const long long n16 = (long long)(bytes / 16);
+  const long long per_round = 256LL * 4;
+  long long grid = (n16 + per_round - 1) / per_round;
+  if (grid > 8LL * cus) grid = 8LL * cus;
+  long long n = n16;
+  void* args[] = {&buf, &n, &sink};
+  hipError_t e = hipLaunchKernel(vat::read_probe_kernel(), dim3((unsigned)grid, 1, 1), dim3(256, 1, 1),
+                                 args, 0, (hipStream_t)stream);
+  return e == hipSuccess ? VAT_OK : VAT_ERR_HIP;
 }
 
 const char* vat_status_string(vat_status_t status) {

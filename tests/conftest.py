@@ -14,8 +14,11 @@ def pytest_configure(config):
 
 
 @pytest.fixture(scope="session")
-def gpu_lib():
-    """The built HIP library, loaded through the C-ABI binding; fails loudly if absent."""
+def gpu_lib(oracle_pool):
+    """The built HIP library, loaded through the C-ABI binding; fails loudly if absent.
+
+    Depends on the oracle pool so that its worker processes start before this
+    process initialises the GPU."""
     import torch
 
     if not torch.cuda.is_available():
@@ -24,3 +27,12 @@ def gpu_lib():
 
     binding.load()  # raises if the shared library is missing
     return binding
+
+
+@pytest.fixture(scope="session")
+def oracle_pool():
+    """Worker processes running the oracle over (request, KV head) items."""
+    from tests.oracle_pool import OraclePool
+
+    with OraclePool() as pool:
+        yield pool

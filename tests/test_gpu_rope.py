@@ -14,7 +14,7 @@ import torch
 
 from oracle import append_kv as oracle_append
 from oracle import verify_attention as oracle_attention
-from tests.gpu_helpers import compare, oracle_of, rows_of, run_gpu, say, to_device, to_f64
+from tests.gpu_helpers import compare, oracle_of, run_gpu, say, to_device, to_f64
 from workloads import make_append_inputs, make_case, make_config, rope_cos_sin, rope_positions
 
 pytestmark = pytest.mark.gpu
@@ -39,16 +39,15 @@ def _oracle(p, cs, requests=None):
                             mask_layout=p.mask_layout, q_cos_sin=cs)
 
 
-@pytest.mark.parametrize("cid", [2, 3, 5, 6, 7])
-def test_query_rope_on_the_workloads(gpu_lib, cid):
+@pytest.mark.parametrize("cid", [2, 3, 4, 5, 6, 7])
+def test_query_rope_on_the_workloads(gpu_lib, oracle_pool, cid):
+    """Every request against the oracle with rotation (spread over host cores)."""
     p = make_config(cid)
     cs = rope_cos_sin(rope_positions(p), p.head_dim)
     say(f"[rope config {cid}] {p.name}")
     got = _rope_run(gpu_lib, p, cs)
-    requests = [0, p.batch - 1] if cid == 7 else None
-    ref = _oracle(p, cs, requests)
-    rows = None if requests is None else rows_of(p, requests)
-    eo, el = compare(p, *to_f64(*got), *ref, rows=rows, what=f"rope config {cid}")
+    ref = oracle_pool.run(p, q_cos_sin=cs)
+    eo, el = compare(p, *to_f64(*got), *ref, what=f"rope config {cid}")
     say(f"  max|out err| {eo:.3e} max|lse err| {el:.3e}")
 
 
