@@ -222,6 +222,30 @@ vat_status_t verify_attention_rope(const vat_problem_t* problem, const void* q,
                                    float v_scale, void* out, float* lse, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* Largest workspace verify_attention_noalloc can serve (64 MiB). */
+#define VAT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* verify_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same plan and kernels, with the workspace taken from a
+ * static device array of VAT_NOALLOC_SCRATCH_BYTES that the library holds
+ * on each GPU it runs on until the process ends (its device address is
+ * looked up on the first call on each device). Arguments and results as
+ * verify_attention, without workspace and workspace_bytes. Returns
+ * VAT_ERR_WORKSPACE, enqueueing nothing, when vat_workspace_size() of the
+ * problem exceeds VAT_NOALLOC_SCRATCH_BYTES. Calls no hipMalloc, hipFree or
+ * allocating routine. Every call on a GPU shares that GPU's one array, which
+ * keeps the last call's contents: calls that overlap on one GPU (on
+ * different streams, or graphs replayed concurrently) race and give
+ * unspecified results; calls in one stream's order are safe. */
+vat_status_t verify_attention_noalloc(const vat_problem_t* problem, const void* q,
+                                      const void* k_cache, const void* v_cache,
+                                      const int32_t* kv_indptr, const int32_t* kv_indices,
+                                      const int32_t* last_page_len, const int32_t* qo_indptr,
+                                      const uint8_t* mask, const int32_t* mask_indptr,
+                                      float sm_scale, float k_scale, float v_scale, void* out,
+                                      float* lse, void* stream);
+
 /* The two halves of verify_attention, for timing each kernel on its own
  * stream position. vat_launch_partial enqueues the partial kernel only (in a
  * direct plan it writes out and lse); vat_launch_merge enqueues the merge

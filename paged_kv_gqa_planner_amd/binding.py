@@ -89,6 +89,8 @@ def load(path: Optional[str] = None):
     lib.vat_append_kv.argtypes = [P(VatProblem), ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp,
                                   f, f, vp]
     lib.vat_append_kv.restype = ctypes.c_int
+    lib.verify_attention_noalloc.argtypes = full[:15] + [vp]
+    lib.verify_attention_noalloc.restype = ctypes.c_int
     lib.vat_read_probe.argtypes = [vp, ctypes.c_size_t, vp, vp]
     lib.vat_read_probe.restype = ctypes.c_int
     lib.vat_status_string.argtypes = [ctypes.c_int]
@@ -265,6 +267,40 @@ def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, 
         _check(lib.verify_attention(*head, *tail), "verify_attention")
     else:
         _check(lib.verify_attention_rope(*head, _ptr(q_cos_sin), *tail), "verify_attention_rope")
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def verify_attention_noalloc(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
+                             qo_indptr, mask=None, mask_indptr=None,
+                             sm_scale: Optional[float] = None, k_scale: float = 1.0,
+                             v_scale: float = 1.0, max_qo_len: Optional[int] = None, out=None,
+                             lse=None, num_cus: int = 0, stream=None, mask_layout: str = "bits"):
+    """``verify_attention`` through the C entry point that allocates nothing:
+    its workspace is the library's static per-device scratch array. ``out``
+    and ``lse`` are allocated here when not given."""
+    import torch
+
+    lib = load()
+    idx = [("kv_indptr", kv_indptr), ("kv_indices", kv_indices), ("last_page_len", last_page_len),
+           ("qo_indptr", qo_indptr), ("mask", mask), ("mask_indptr", mask_indptr)]
+    _check_tensors(q, k_cache, v_cache, idx)
+    problem = problem_from_tensors(q, k_cache, kv_indptr, kv_indices, mask, max_qo_len,
+                                   num_cus=num_cus, mask_layout=mask_layout)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[2])
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    st = lib.verify_attention_noalloc(
+        ctypes.byref(problem), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_indptr),
+        _ptr(kv_indices), _ptr(last_page_len), _ptr(qo_indptr), _ptr(mask), _ptr(mask_indptr),
+        float(sm_scale), float(k_scale), float(v_scale), _ptr(out), _ptr(lse),
+        _stream_handle(stream))
+    _check(st, "verify_attention_noalloc")
     return out, lse
 
 

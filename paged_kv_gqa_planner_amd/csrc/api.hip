@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "plan.h"
 #include "verify_attention.h"
 
@@ -23,6 +25,30 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 int g_cu_count[kMaxDevices];  // 0 = not yet queried
+
+// Workspace of verify_attention_noalloc: one static array in each device's
+// copy of the code object, zero at load and held until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory; its
+// device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is used.
+constexpr size_t kScratchBytes = VAT_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch keeps the workspace's 256-byte alignment");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+std::mutex g_scratch_mu;
+
+vat_status_t device_scratch(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return VAT_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return VAT_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return VAT_OK;
+}
 
 vat_status_t device_cus(int32_t* cus) {
   int dev = 0;
@@ -362,6 +388,34 @@ vat_status_t verify_attention_rope(const vat_problem_t* problem, const void* q,
   if (st != VAT_OK) return st;
   return launch_merge(problem, plan, kv_indptr, last_page_len, qo_indptr, v_scale, out, lse,
                       workspace, (hipStream_t)stream);
+}
+
+vat_status_t verify_attention_noalloc(const vat_problem_t* problem, const void* q,
+                                      const void* k_cache, const void* v_cache,
+                                      const int32_t* kv_indptr, const int32_t* kv_indices,
+                                      const int32_t* last_page_len, const int32_t* qo_indptr,
+                                      const uint8_t* mask, const int32_t* mask_indptr,
+                                      float sm_scale, float k_scale, float v_scale, void* out,
+                                      float* lse, void* stream) {
+  vat_plan_t plan;
+  vat_status_t st = plan_for(problem, &plan);
+  if (st != VAT_OK) return st;
+  if ((uint64_t)plan.workspace_bytes > (uint64_t)kScratchBytes) return VAT_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (plan.workspace_bytes > 0 && !plan_is_empty(plan)) {
+    st = device_scratch(&ws);
+    if (st != VAT_OK) return st;
+  }
+  st = prepare(problem, q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr,
+               mask, mask_indptr, nullptr, sm_scale, k_scale, v_scale, out, lse, ws,
+               ws ? kScratchBytes : 0, &plan);
+  if (st != VAT_OK || plan_is_empty(plan)) return st;
+  st = launch_partial(problem, plan, q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len,
+                      qo_indptr, mask, mask_indptr, nullptr, sm_scale, k_scale, v_scale, out,
+                      lse, ws, (hipStream_t)stream);
+  if (st != VAT_OK) return st;
+  return launch_merge(problem, plan, kv_indptr, last_page_len, qo_indptr, v_scale, out, lse, ws,
+                      (hipStream_t)stream);
 }
 
 vat_status_t vat_append_kv(const vat_problem_t* problem, int32_t src_dtype, const void* k_new,

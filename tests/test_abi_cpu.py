@@ -513,3 +513,15 @@ def test_read_probe_host_checks(lib):
     assert lib.vat_read_probe(vp(4096), 72, vp(8192), None) == 2   # not a multiple of 16
     assert lib.vat_read_probe(vp(4104), 64, vp(8192), None) == 4   # buffer misaligned
     assert lib.vat_read_probe(vp(4096), 64, vp(8194), None) == 4   # sink misaligned
+
+
+def test_noalloc_refuses_an_oversized_workspace_on_the_host(lib):
+    """verify_attention_noalloc checks the planned workspace against its static
+    array before anything else touches the device."""
+    prob = B.make_problem(batch=1, num_qo_heads=64, num_kv_heads=1, head_dim=128, page_size=16,
+                          num_pages=1 << 16, num_kv_indices=1 << 16, num_qo_tokens=64,
+                          max_qo_len=64, q_dtype=1, kv_dtype=1, has_mask=0, num_cus=4096)
+    assert B.vat_workspace_size(prob) > B.NOALLOC_SCRATCH_BYTES
+    st = lib.verify_attention_noalloc(ctypes.byref(prob), *([None] * 9), 0.1, 1.0, 1.0, None,
+                                      None, None)
+    assert st == 5
