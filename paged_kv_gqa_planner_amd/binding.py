@@ -37,7 +37,7 @@ class VatPlan(ctypes.Structure):
         "rows_per_block", "row_blocks", "chunk_keys", "num_chunk_ids", "grid_x", "grid_y",
         "threads", "lds_bytes", "merge_grid", "merge_threads", "num_cus")] + [
         ("workspace_bytes", ctypes.c_int64), ("block_order", ctypes.c_int32),
-        ("merge_rows", ctypes.c_int32)]
+        ("merge_rows", ctypes.c_int32), ("heads_per_group", ctypes.c_int32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

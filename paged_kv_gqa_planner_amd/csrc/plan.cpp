@@ -103,6 +103,48 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   const int64_t D = p->head_dim;
   const int64_t eb = elem_bytes(p->kv_dtype);
 
+  // Two KV heads per workgroup: fp8 caches with D = 128 (128-byte head
+  // rows) and an even head count, every head's rows in at most two tiles, a
+  // batch the balanced slices serve, no RoPE and no byte-row masks. A key's
+  // DMA then reads both heads' rows as one 256-byte run instead of two
+  // 128-byte runs 128 bytes apart, each fetched by another workgroup at
+  // another time. Computing waves: one tile each, the tiles of head h, then
+  // those of h + 1; four DMA waves; 64-key stages of 32 KB.
+  const bool fp8 = p->kv_dtype == VAT_FP8_E4M3FN;
+  if (fp8 && D == 128 && p->num_kv_heads % 2 == 0 && tiles <= 2 && !p->rope &&
+      p->has_mask != 2 && p->chunk_keys == -1 && p->batch <= kSliceMaxBatch) {
+    const int64_t M = tiles * 16;
+    const int64_t groups = p->num_kv_heads / 2;
+    plan->kernel = 1;
+    plan->heads_per_group = 2;
+    plan->threads = kStreamThreads;
+    plan->row_tiles_per_wave = 1;
+    plan->waves_rows = int32_t(2 * tiles);
+    plan->waves_keys = 1;
+    plan->dma_waves = 4;
+    plan->rows_per_block = int32_t(M);
+    plan->row_blocks = 1;
+    plan->stages = 4;
+    plan->lds_bytes = 4 * 2 * 64 * 256 + kStreamPageWindow * 4;
+    int64_t nx = int64_t(num_cus) / groups;
+    if (nx < 1) nx = 1;
+    plan->slices = int32_t(nx);
+    plan->direct = nx == 1 ? 1 : 0;
+    plan->chunk_keys = 0;
+    plan->num_chunk_ids = int32_t(nx + p->batch);  // partial slots: slice + request
+    plan->grid_x = int32_t(nx);
+    plan->grid_y = int32_t(groups);
+    if (plan->direct) return VAT_OK;
+    plan->merge_rows = merge_rows_for(nx / p->batch + 1, D);
+    const int64_t row_groups = cdiv(M, plan->merge_rows);
+    plan->merge_grid = int32_t(int64_t(p->batch) * p->num_kv_heads * row_groups);
+    const int64_t parts = (nx + p->batch) * p->num_kv_heads;
+    const int64_t lse_off = cdiv(parts * M * D * 4, 256) * 256;
+    plan->workspace_bytes = lse_off + cdiv(parts * M * 4, 256) * 256;
+    return VAT_OK;
+  }
+  plan->heads_per_group = 1;
+
   // Kernel and row tiling.
   //  * Streaming kernel (bf16 / fp8 caches): wave w of eight computes row
   //    tiles [w rt, w rt + rt) of a row block over all of the block's keys
@@ -114,7 +156,6 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   int rt, wr, wk;
   // fp8 caches with D = 64 have too few 1 KB loads per stage for eight waves;
   // with fp8 the decode registers leave room for one row tile per wave.
-  const bool fp8 = p->kv_dtype == VAT_FP8_E4M3FN;
   const bool stream = (p->kv_dtype != VAT_F32) && !(fp8 && p->head_dim == 64);
   int dw = 0;
   if (stream) {

@@ -37,10 +37,13 @@ constexpr int kSWaves = kStreamThreads / 64;  // 8
 
 // DW: waves issuing the DMA (2 or 4: the last ones of eight; 8: all of them);
 // SK: keys per stage.
-template <int KV, int D, int DW = kSWaves, int SK = kStageKeys>
+// HP: KV heads per workgroup (1, or 2 adjacent heads whose rows lie side by
+// side in each slot, so a key row in LDS is both heads' rows).
+template <int KV, int D, int DW = kSWaves, int SK = kStageKeys, int HP = 1>
 struct StreamGeom {
   static constexpr int EB = (KV == KV_E4M3) ? 1 : 2;  // bytes per cache element
-  static constexpr int ROW = D * EB;                   // bytes per key row
+  static constexpr int HROW = D * EB;                  // bytes of one head's key row
+  static constexpr int ROW = HP * HROW;                // bytes per key row in LDS
   static constexpr int CPK = ROW / 16;                 // 16-byte chunks per key row
   static constexpr int KPI = 64 / CPK;                 // keys per 1 KB DMA instruction
   static constexpr int NINST = SK / KPI;               // DMA instructions per K (or V) block
@@ -56,6 +59,23 @@ struct StreamGeom {
 // chunk, or four keys at two chunks) fall in distinct banks.
 template <int CPK>
 __device__ __forceinline__ int swz(int kl, int c) { return c ^ (kl & (CPK - 1)); }
+
+// Where compute_stage finds 16-byte chunk `ch` of key `kl`'s row (of the
+// wave's KV head) within a stage's K block, and where the V block starts.
+// Per-head stages (vat_stream) hold one KV head's rows, one after another,
+// chunks swizzled by swz().
+// With two heads per workgroup a key row holds both heads' rows; `hc` is
+// the wave's head's first chunk in it.
+template <int KV, int D, int SK, int HP = 1>
+struct HeadLayout {
+  static constexpr int ROW = StreamGeom<KV, D, kStreamThreads / 64, SK, HP>::ROW;
+  static constexpr int CPK = ROW / 16;
+  static constexpr int VBLK = SK * ROW;
+  int hc = 0;
+  __device__ __forceinline__ int off(int kl, int ch) const {
+    return kl * ROW + (swz<CPK>(kl, hc + ch) << 4);
+  }
+};
 
 // Max / sum over the four lanes l, l^16, l^32, l^48 of one query row, on the
 // VALU: permlane16/32_swap hand each lane its partner's value.
@@ -90,14 +110,14 @@ __device__ __forceinline__ unsigned cvt_pk_bf16(float lo, float hi) {
 // Issue this wave's share of the DMA loads of one stage: keys n0 .. n0 + 63,
 // each clamped to `last` (the item's last key) so every address is a real
 // cached entry; keys past the item are masked out of the softmax later.
-template <int KV, int D, int DW, int SK>
+template <int KV, int D, int DW, int SK, int HP>
 __device__ __forceinline__ void issue_stage(const PartialArgs& a, const int* win, int win_base,
                                             int last_rel, int h, int n0, int last,
                                             unsigned char* stage, int dw, int lane,
                                             bool uniform_pages) {
-  using G = StreamGeom<KV, D, DW, SK>;
+  using G = StreamGeom<KV, D, DW, SK, HP>;
   const int ps_mask = (1 << a.page_shift) - 1;
-  const long long page_bytes = (long long)G::ROW * a.hkv << a.page_shift;
+  const long long page_bytes = (long long)G::HROW * a.hkv << a.page_shift;
   int pg[G::IPW];
 #pragma unroll
   for (int ii = 0; ii < G::IPW; ++ii) {
@@ -113,7 +133,8 @@ __device__ __forceinline__ void issue_stage(const PartialArgs& a, const int* win
     const int kl = i * G::KPI + lane / G::CPK;
     const int c = swz<G::CPK>(kl, lane % G::CPK);
     const int n = min(n0 + kl, last);
-    const unsigned off = (unsigned)(((n & ps_mask) * a.hkv + h) * G::ROW + c * 16);
+    // Heads h .. h + HP - 1 of the key's slot, side by side.
+    const unsigned off = (unsigned)(((n & ps_mask) * a.hkv + h) * G::HROW + c * 16);
     const unsigned char* kb;
     const unsigned char* vb;
     if (uniform_pages) {
@@ -195,14 +216,13 @@ __device__ __forceinline__ unsigned long long visible_bits(unsigned long long bi
 // stage.
 // QLO: the queries are carried as two bf16 terms (qf + qlo, a rotated query
 // that bf16 alone would round), and S^T takes one MFMA per term.
-template <int KV, int D, int RT, int KT, int SK = kStageKeys, bool QLO = false>
+template <int KV, int D, int RT, int KT, int SK, bool QLO, class LAY>
 __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsigned (&qf)[RT][D / 8],
                                               const unsigned (&qlo)[RT][QLO ? D / 8 : 1],
                                               const int (&row_t)[RT],
                                               const unsigned long long (&row_bits)[RT],
                                               const Vis& vis, const unsigned char* stage, int n0,
-                                              float c, int lane, int kt0) {
-  using G = StreamGeom<KV, D, kSWaves, SK>;
+                                              float c, int lane, int kt0, const LAY& lay) {
   static_assert(KT == 2 || KT == 4 || KT == 8, "one to four 32-key blocks");
   // Two row tiles per wave: the scheduler interleaves the stage's LDS reads
   // with its MFMAs (one-tile variants run faster with the default schedule).
@@ -226,12 +246,11 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
       u32x4 kw4;
       if constexpr (KV == KV_E4M3) {
         const int ch = 4 * (ks >> 1) + j4;
-        const u32x2 raw =
-            *(const u32x2*)(stage + klk * G::ROW + (swz<G::CPK>(klk, ch) << 4) + 8 * (ks & 1));
+        const u32x2 raw = *(const u32x2*)(stage + lay.off(klk, ch) + 8 * (ks & 1));
         kw4 = e4m3x8_to_bf16(raw.x, raw.y);
       } else {
         const int ch = 4 * ks + j4;
-        kw4 = *(const u32x4*)(stage + klk * G::ROW + (swz<G::CPK>(klk, ch) << 4));
+        kw4 = *(const u32x4*)(stage + lay.off(klk, ch));
       }
       ka[kt] = __builtin_bit_cast(bf16x8, kw4);
     }
@@ -339,7 +358,7 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
                                                    __builtin_bit_cast(bf16x8, u32x4{b0.x, b0.y, b1.x, b1.y}),
                                                    c, 0, 0, 0);
   };
-  const unsigned char* vb = stage + G::BLK;
+  const unsigned char* vb = stage + LAY::VBLK;
   constexpr int NB = KT / 2;  // 32-key blocks
   if constexpr (KV == KV_E4M3) {
     // One 8-bit transpose read per (32-key block, d tile): source lane s of
@@ -350,7 +369,7 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
     auto vaddr8 = [&](int kb, int dt) {
       const int e = l16 >> 1;
       const int kl = 16 * (kt0 + 2 * kb + (e >> 2)) + 4 * j4 + (e & 3);
-      return vb + kl * G::ROW + (swz<G::CPK>(kl, dt) << 4) + 8 * (l16 & 1);
+      return vb + lay.off(kl, dt) + 8 * (l16 & 1);
     };
     u32x2 raw[2][NDT];
 #pragma unroll
@@ -392,7 +411,7 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
     auto vaddr = [&](int kt, int dt) {
       const int kl = 16 * (kt0 + kt) + klb;
       const int d0 = 16 * dt + 4 * (l16 & 3);
-      return vb + kl * G::ROW + (swz<G::CPK>(kl, d0 >> 3) << 4) + (d0 & 7) * 2;
+      return vb + lay.off(kl, d0 >> 3) + (d0 & 7) * 2;
     };
     constexpr bool kAhead = RT == 1;  // registers for a third tile of reads
     constexpr int NBUF = kAhead ? 2 : 1;
@@ -720,9 +739,12 @@ __device__ __forceinline__ void merge_pair_state(StreamAcc<D, RT>& acc, float (&
 // through one ring of LDS buffers filled by DMA. Wave w < waves_rows owns row
 // tiles [w RT, w RT + RT) of every segment and runs all of its keys, so no
 // two waves ever hold parts of the same row; all eight waves issue the DMA.
-template <int KV, int D, int RT, int NS, int DW, int P, int SK, bool ROWS, bool ROPE>
+// HP = 2: the workgroup takes two adjacent KV heads, h and h + 1, whose rows
+// sit side by side in every slot, so each key's DMA reads one run of both
+// heads' rows; computing waves take the row tiles of h, then those of h + 1.
+template <int KV, int D, int RT, int NS, int DW, int P, int SK, bool ROWS, bool ROPE, int HP = 1>
 __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
-  using G = StreamGeom<KV, D, DW, SK>;
+  using G = StreamGeom<KV, D, DW, SK, HP>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   int* win = (int*)(smem + NS * G::STAGE);
   const int lane = threadIdx.x & 63;
@@ -749,7 +771,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
     if (a.block_order == 2 && k < rb) rb2 = k;
   } else {
     item = (int)blockIdx.x;
-    h = blockIdx.y / a.row_blocks;
+    h = HP * (int)(blockIdx.y / a.row_blocks);  // first KV head of the workgroup
     rb = a.row_blocks - 1 - (int)(blockIdx.y % a.row_blocks);
   }
   const int shift = a.page_shift;
@@ -860,7 +882,9 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   const bool computes = wave < ncomp;
   const int tset = wave % a.waves_rows;
   const int phase = wave / a.waves_rows;
-  const int row0 = tset * RT * 16;  // within the row block
+  const int tph = a.waves_rows / HP;          // tile sets per KV head
+  const int hw = h + tset / tph;              // the wave's KV head
+  const int row0 = (tset % tph) * RT * 16;    // within the row block
   int rbase = row0;                   // in the request's rows (set per segment)
   float* pair_slot = (float*)(smem + NS * G::STAGE + kStreamPageWindow * 4) + tset * PairSlot<D, RT>::FLOATS;
   RowSet<KV, D, RT, ROWS, ROPE> rs;
@@ -873,7 +897,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
     seg_L = lane_val(sg.L, s);
     has_rows = rbase < a.group * seg_L;
     rs.fetch(a, lane_val(sg.q_start, s), seg_L, lane_val(sg.prefix, s), lane_val(sg.mask_off, s),
-             rbase, h, lane);
+             rbase, hw, lane);
     vis.hi = lane_val(sg.hi, s);
     vis.masked_from = lane_val(sg.prefix, s);
     vis.t_min = rbase / a.group;
@@ -914,7 +938,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
       __syncthreads();
     }
     if (dma)
-      issue_stage<KV, D, DW, SK>(a, win, wbase - woff, min(wcount - 1 - wbase, kStreamPageWindow - 1), h,
+      issue_stage<KV, D, DW, SK, HP>(a, win, wbase - woff, min(wcount - 1 - wbase, kStreamPageWindow - 1), h,
                              n0, last, smem + buf * G::STAGE, dw, lane, uniform_pages);
   };
 
@@ -952,8 +976,8 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
       const int n0 = lane_val(sg.lo, s) + (g - first) * SK;
       const unsigned char* stage = smem + (g % NS) * G::STAGE;
       compute_stage<KV, D, RT, SK / 16 / P, SK, ROPE>(acc, rs.qf, rs.qlo, rs.row_t, rs.row_bits, vis,
-                                                      stage, n0,
-                                                a.c_log2, lane, phase * (SK / 16 / P));
+                                                      stage, n0, a.c_log2, lane, phase * (SK / 16 / P),
+                                                      HeadLayout<KV, D, SK, HP>{(hw - h) * (G::HROW / 16)});
     }
     if (g == lane_val(sg.incl, s) - 1) {
       // The segment's last stage (every wave sees it).
@@ -968,7 +992,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
       }
       if (computes && has_rows && phase == 0)
         write_rows<KV, D, RT, ROWS, ROPE>(acc, lrow, rs, a, lane_val(sg.q_start, s), lane_val(sg.whole, s) != 0,
-                              lane_val(sg.slot, s), lane_val(sg.rb, s), row0, h, lane);
+                              lane_val(sg.slot, s), lane_val(sg.rb, s), row0, hw, lane);
     }
   }
 }
@@ -1004,7 +1028,11 @@ static const void* stream_variant(int rt, int dma_waves, int pair, bool rows, bo
 }
 
 const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int pair,
-                          int mask_mode, int rope) {
+                          int mask_mode, int rope, int heads_per_group) {
+  // Two fp8 heads of D 128 per workgroup: 256-byte key rows, 64-key stages,
+  // one row tile per computing wave, four DMA waves.
+  if (heads_per_group == 2)
+    return (const void*)vat_stream<KV_E4M3, 128, 1, 4, 4, 1, 64, false, false, 2>;
   static_assert(stream_stage_keys(KV_BF16, 128) == 64 && stream_stage_keys(KV_BF16, 64) == 128 &&
                 stream_stage_keys(KV_E4M3, 128) == 128, "stage sizes match the planner");
   const bool rows = mask_mode == 2, ro = rope != 0;

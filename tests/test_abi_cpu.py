@@ -43,7 +43,7 @@ def test_library_exports_every_header_function(lib):
             "vat_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.vat_abi_version() == 4
+    assert lib.vat_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -85,11 +85,13 @@ def test_plans_for_the_workloads(lib, cid):
         assert plan.grid_y == 1
         assert plan.grid_x == 8 * w * -(-groups // 8)
     else:
-        assert plan.grid_y == p.num_kv_heads * plan.row_blocks
+        hp = plan.heads_per_group
+        assert plan.grid_y == p.num_kv_heads // hp * plan.row_blocks
     if plan.slices:
-        # Balanced slices: one workgroup per (slice, KV head), CU-filling.
+        # Balanced slices: one workgroup per (slice, KV head group), CU-filling.
+        hp = plan.heads_per_group
         assert plan.kernel == 1 and plan.chunk_keys == 0
-        assert plan.slices == max(1, 256 // p.num_kv_heads) == plan.grid_x
+        assert plan.slices == max(1, 256 // (p.num_kv_heads // hp)) == plan.grid_x
         assert plan.num_chunk_ids == plan.slices + p.batch
     else:
         assert plan.chunk_keys % 16 == 0 and plan.chunk_keys > 0
@@ -106,6 +108,12 @@ def test_plans_for_the_workloads(lib, cid):
         # Wide trees: 512 rows per KV head in two blocks, chunked prefixes.
         assert plan.kernel == 1 and plan.rows_per_block == 256 and plan.row_blocks == 2
         assert plan.slices == 0 and plan.block_order == 1
+    elif cid == 5:
+        # fp8 of D 128, 32 rows per KV head: two heads per workgroup, one row
+        # tile per computing wave (four), four DMA waves.
+        assert plan.kernel == 1 and plan.heads_per_group == 2 and plan.row_tiles_per_wave == 1
+        assert plan.rows_per_block == 32 and plan.waves_rows == 4 and plan.dma_waves == 4
+        assert plan.slices == 64 and plan.grid_y == 4
     else:
         assert plan.kernel == 1 and plan.threads == 512 and plan.slices > 0
     if not plan.direct:
@@ -299,6 +307,25 @@ def test_slice_segments_cover_each_request_once():
             # The merge reads exactly the slots written as partials; a request
             # inside one slice is written directly.
             assert merged[b] == [m[2] for m in mine]
+
+
+def test_two_heads_per_workgroup_only_where_the_shape_fits(lib):
+    """fp8 caches of D 128 with an even KV-head count, at most 32 rows per KV
+    head, planner-chosen slices, no RoPE, no byte-row masks: two heads per
+    workgroup; everything else one."""
+    fp8 = dict(kv_dtype=2, num_kv_heads=8, num_qo_heads=32, max_qo_len=8, num_qo_tokens=16)
+    assert B.vat_plan(base_problem(**fp8)).heads_per_group == 2
+    assert B.vat_plan(base_problem(**{**fp8, "num_kv_heads": 2, "num_qo_heads": 8})).heads_per_group == 2
+    plan = B.vat_plan(base_problem(**{**fp8, "max_qo_len": 4}))
+    assert plan.heads_per_group == 2 and plan.waves_rows == 2
+    assert B.vat_plan(base_problem(**{**fp8, "has_mask": 1, "num_mask_bytes": 16})).heads_per_group == 2
+    for change in (dict(max_qo_len=9, num_qo_tokens=18), dict(num_kv_heads=1, num_qo_heads=4),
+                   dict(num_kv_heads=3, num_qo_heads=12), dict(head_dim=64), dict(kv_dtype=1),
+                   dict(rope=1), dict(chunk_keys=64), dict(has_mask=2, num_mask_bytes=64),
+                   dict(batch=65, num_qo_tokens=65, max_qo_len=1, num_kv_indices=65)):
+        assert B.vat_plan(base_problem(**{**fp8, **change})).heads_per_group == 1, change
+    plan = B.vat_plan(base_problem(**{**fp8, "num_cus": 4}))
+    assert plan.heads_per_group == 2 and plan.direct == 1 and plan.workspace_bytes == 0
 
 
 @pytest.mark.parametrize("kw,code", [
