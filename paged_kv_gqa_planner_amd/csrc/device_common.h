@@ -42,6 +42,15 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
   return v;
 }
+// The same read at LDS byte address `addr + OFF`, OFF in the instruction's
+// immediate offset field (no address arithmetic per read).
+template <int OFF>
+__device__ __forceinline__ s16x4 lds_read_tr16_at(unsigned addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+  s16x4 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+  return v;
+}
 
 // Wait until at most N LDS/scalar-memory operations are outstanding (LDS
 // operations complete in order, so the reads issued before the last N have
@@ -58,6 +67,13 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const void* p) {
   u32x2 v;
   const unsigned addr = (unsigned)(uintptr_t)(const lds_void_t*)p;
   asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr8_at(unsigned addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
   return v;
 }
 

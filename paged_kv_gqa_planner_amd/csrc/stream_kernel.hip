@@ -71,6 +71,11 @@ struct HeadLayout {
   static constexpr int ROW = StreamGeom<KV, D, kStreamThreads / 64, SK, HP>::ROW;
   static constexpr int CPK = ROW / 16;
   static constexpr int VBLK = SK * ROW;
+  // Key kl + 16 m sits 16 m rows after key kl at the same swizzled chunk
+  // (the swizzle reads kl % CPK, CPK <= 16), so the per-lane part of an
+  // address is the same for every 16-key tile.
+  static constexpr int KT_STRIDE = 16 * ROW;
+  static_assert(CPK <= 16, "tile-invariant swizzle");
   int hc = 0;
   __device__ __forceinline__ int off(int kl, int ch) const {
     return kl * ROW + (swz<CPK>(kl, hc + ch) << 4);
@@ -358,7 +363,6 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
                                                    __builtin_bit_cast(bf16x8, u32x4{b0.x, b0.y, b1.x, b1.y}),
                                                    c, 0, 0, 0);
   };
-  const unsigned char* vb = stage + LAY::VBLK;
   constexpr int NB = KT / 2;  // 32-key blocks
   if constexpr (KV == KV_E4M3) {
     // One 8-bit transpose read per (32-key block, d tile): source lane s of
@@ -366,14 +370,19 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
     // d = 16 dt + 8 (s % 2) ..; lane (d, j) then receives the codes of k
     // indices 8 j .. 8 j + 7 at d, decoded exactly to bf16 in registers.
     // Block kb + 1's reads are in flight while block kb's MFMAs run.
-    auto vaddr8 = [&](int kb, int dt) {
+    // Per-lane address of d tile dt in 32-key block 0; block kb adds the
+    // immediate 2 kb KT_STRIDE.
+    unsigned vbase[NDT];
+    {
       const int e = l16 >> 1;
-      const int kl = 16 * (kt0 + 2 * kb + (e >> 2)) + 4 * j4 + (e & 3);
-      return vb + lay.off(kl, dt) + 8 * (l16 & 1);
-    };
+      const int klx = 16 * (e >> 2) + 4 * j4 + (e & 3);
+      const unsigned sb = (unsigned)(uintptr_t)(const lds_void_t*)stage + kt0 * LAY::KT_STRIDE;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) vbase[dt] = sb + lay.off(klx, dt) + 8 * (l16 & 1);
+    }
     u32x2 raw[2][NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) raw[0][dt] = lds_read_tr8(vaddr8(0, dt));
+    for (int dt = 0; dt < NDT; ++dt) raw[0][dt] = lds_read_tr8_at<LAY::VBLK>(vbase[dt]);
     [&]<int... K>(std::integer_sequence<int, K...>) {
       (
           [&] {
@@ -381,7 +390,8 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
             constexpr bool more = kb + 1 < NB;
             if constexpr (more) {
 #pragma unroll
-              for (int dt = 0; dt < NDT; ++dt) raw[(kb + 1) & 1][dt] = lds_read_tr8(vaddr8(kb + 1, dt));
+              for (int dt = 0; dt < NDT; ++dt)
+                raw[(kb + 1) & 1][dt] = lds_read_tr8_at<LAY::VBLK + 2 * (kb + 1) * LAY::KT_STRIDE>(vbase[dt]);
             }
             [&]<int... I>(std::integer_sequence<int, I...>) {
               ((lds_wait_tied<(more ? NDT : 0) + NDT - 1 - I>(raw[kb & 1][I]),
@@ -407,27 +417,35 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
     // second tile, and with one row tile block kb + 1's first, are requested
     // before block kb's MFMAs; each MFMA waits only for its own reads (LDS
     // reads complete in order).
-    const int klb = 4 * j4 + (l16 >> 2);
-    auto vaddr = [&](int kt, int dt) {
-      const int kl = 16 * (kt0 + kt) + klb;
-      const int d0 = 16 * dt + 4 * (l16 & 3);
-      return vb + lay.off(kl, d0 >> 3) + (d0 & 7) * 2;
-    };
+    // Per-lane address of d tile dt in key tile 0; tile kt adds the
+    // immediate kt KT_STRIDE.
+    unsigned vbase[NDT];
+    {
+      const int klb = 4 * j4 + (l16 >> 2);
+      const unsigned sb = (unsigned)(uintptr_t)(const lds_void_t*)stage + kt0 * LAY::KT_STRIDE;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int d0 = 16 * dt + 4 * (l16 & 3);
+        vbase[dt] = sb + lay.off(klb, d0 >> 3) + (d0 & 7) * 2;
+      }
+    }
     constexpr bool kAhead = RT == 1;  // registers for a third tile of reads
     constexpr int NBUF = kAhead ? 2 : 1;
     s16x4 va[NBUF][NDT], vv[NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) va[0][dt] = lds_read_tr16(vaddr(0, dt));
+    for (int dt = 0; dt < NDT; ++dt) va[0][dt] = lds_read_tr16_at<LAY::VBLK>(vbase[dt]);
     [&]<int... K>(std::integer_sequence<int, K...>) {
       (
           [&] {
             constexpr int kb = K;
             constexpr bool ahead = kAhead && kb + 1 < NB;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) vv[dt] = lds_read_tr16(vaddr(2 * kb + 1, dt));
+            for (int dt = 0; dt < NDT; ++dt)
+              vv[dt] = lds_read_tr16_at<LAY::VBLK + (2 * kb + 1) * LAY::KT_STRIDE>(vbase[dt]);
             if constexpr (ahead) {
 #pragma unroll
-              for (int dt = 0; dt < NDT; ++dt) va[(kb + 1) % NBUF][dt] = lds_read_tr16(vaddr(2 * kb + 2, dt));
+              for (int dt = 0; dt < NDT; ++dt)
+                va[(kb + 1) % NBUF][dt] = lds_read_tr16_at<LAY::VBLK + (2 * kb + 2) * LAY::KT_STRIDE>(vbase[dt]);
             }
             [&]<int... I>(std::integer_sequence<int, I...>) {
               ((lds_wait_tied2<(ahead ? NDT : 0) + NDT - 1 - I>(va[kb % NBUF][I], vv[I]),
@@ -440,7 +458,8 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
             }(std::make_integer_sequence<int, NDT>{});
             if constexpr (!kAhead && kb + 1 < NB) {
 #pragma unroll
-              for (int dt = 0; dt < NDT; ++dt) va[(kb + 1) % NBUF][dt] = lds_read_tr16(vaddr(2 * kb + 2, dt));
+              for (int dt = 0; dt < NDT; ++dt)
+                va[(kb + 1) % NBUF][dt] = lds_read_tr16_at<LAY::VBLK + (2 * kb + 2) * LAY::KT_STRIDE>(vbase[dt]);
             }
           }(),
           ...);

@@ -328,6 +328,7 @@ def test_two_heads_per_workgroup_only_where_the_shape_fits(lib):
     assert plan.heads_per_group == 2 and plan.direct == 1 and plan.workspace_bytes == 0
 
 
+
 @pytest.mark.parametrize("kw,code", [
     (dict(num_qo_heads=6, num_kv_heads=4), 2),
     (dict(head_dim=96), 3),
@@ -552,3 +553,21 @@ def test_noalloc_refuses_an_oversized_workspace_on_the_host(lib):
     st = lib.verify_attention_noalloc(ctypes.byref(prob), *([None] * 9), 0.1, 1.0, 1.0, None,
                                       None, None)
     assert st == 5
+
+
+@pytest.mark.parametrize("kv,hkv,G,L", [(1, 8, 4, 1), (1, 8, 4, 4), (1, 2, 16, 1), (2, 8, 4, 8),
+                                         (2, 4, 4, 2), (1, 8, 4, 5), (1, 8, 8, 17), (2, 1, 4, 8)])
+@pytest.mark.parametrize("batch", [1, 2, 5, 13, 64, 65, 300])
+def test_merge_grid_covers_every_row_of_every_request(lib, kv, hkv, G, L, batch):
+    """Whatever the plan, the merge launches one workgroup per (request, KV head,
+    row block, group of merge_rows rows), so every row that has partials is merged."""
+    prob = base_problem(batch=batch, num_qo_heads=hkv * G, num_kv_heads=hkv, kv_dtype=kv,
+                        max_qo_len=L, num_qo_tokens=batch * L, num_pages=8000,
+                        num_kv_indices=7000)
+    plan = B.vat_plan(prob)
+    if plan.direct:
+        assert plan.merge_grid == 0
+        return
+    assert plan.merge_rows in (4, 16)
+    per_item = -(-plan.rows_per_block // plan.merge_rows)
+    assert plan.merge_grid == batch * hkv * plan.row_blocks * per_item

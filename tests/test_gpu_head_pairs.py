@@ -21,15 +21,15 @@ from workloads import make_case, make_config
 pytestmark = pytest.mark.gpu
 
 
-def _case(seed, B, G, Lmax, ps, mask_kind, prefix_hi=600, empty=False, **kw):
+def _case(seed, B, G, Lmax, ps, mask_kind, prefix_hi=600, empty=False, kv="e4m3", hkv=8, **kw):
     rng = np.random.default_rng(seed)
     lens = [int(x) for x in rng.integers(1, Lmax + 1, size=B)]
     if empty and B > 2:
         lens[1] = 0
     prefixes = [int(x) for x in rng.integers(0, prefix_hi + 1, size=B)]
-    return make_case(seed, prefix_lens=prefixes, qo_lens=lens, num_qo_heads=8 * G,
-                     num_kv_heads=8, head_dim=128, page_size=ps, q_dtype="bf16",
-                     kv_dtype="e4m3", mask_kind=mask_kind, fp8_absmax_scales=True,
+    return make_case(seed, prefix_lens=prefixes, qo_lens=lens, num_qo_heads=hkv * G,
+                     num_kv_heads=hkv, head_dim=128, page_size=ps, q_dtype="bf16",
+                     kv_dtype=kv, mask_kind=mask_kind, fp8_absmax_scales=(kv == "e4m3"),
                      max_qo_len=Lmax, **kw)
 
 
