@@ -113,8 +113,8 @@ typedef struct {
                              KV head and row block writes out directly);
                              > 0: chunk length in keys, multiple of 16 */
   int32_t rope;           /* 0; 1: verify_attention_rope rotates the queries by
-                             RoPE (bf16 caches or fp8 with D 128; not with
-                             full byte-row masks) */
+                             RoPE (bf16 caches, or fp8 with D 128; either mask
+                             layout) */
 } vat_problem_t;
 
 /* What the planner decided; filled by vat_plan. Shape-only: the same problem

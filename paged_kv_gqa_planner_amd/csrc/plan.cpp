@@ -38,9 +38,10 @@ vat_status_t validate_problem(const vat_problem_t* p) {
   if (p->has_mask && p->max_qo_len > kMaxMaskedLen) return VAT_ERR_UNSUPPORTED;
   if (p->has_mask && p->num_mask_bytes < 1) return VAT_ERR_SHAPE;
   if (p->rope != 0 && p->rope != 1) return VAT_ERR_SHAPE;
-  // Query RoPE runs in the streaming kernel, without byte-row masks.
-  if (p->rope && (p->kv_dtype == VAT_F32 ||
-                  (p->kv_dtype == VAT_FP8_E4M3FN && p->head_dim == 64) || p->has_mask == 2))
+  // Query RoPE runs in the streaming kernel: not for fp32 caches (the
+  // row-tiled kernel) nor for fp8 with D = 64, whose query layout puts the
+  // two dimensions of a rotated pair (i, i + D/2) in different lanes.
+  if (p->rope && (p->kv_dtype == VAT_F32 || (p->kv_dtype == VAT_FP8_E4M3FN && p->head_dim == 64)))
     return VAT_ERR_UNSUPPORTED;
   if (p->chunk_keys < -1 || (p->chunk_keys > 0 && p->chunk_keys % kChunkQuantum))
     return VAT_ERR_SHAPE;

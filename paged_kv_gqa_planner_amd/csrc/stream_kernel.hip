@@ -1024,6 +1024,13 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
 // 128 KB the planner gives the ring.
 template <int KV, int D, int NS, int SK>
 static const void* stream_variant(int rt, int dma_waves, int pair, bool rows, bool rope) {
+  if (rope && rows) {
+    // RoPE with full byte-row masks: one row tile per wave.
+    if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK, true, true>;
+    if (dma_waves == 2) return (const void*)vat_stream<KV, D, 1, NS, 2, 1, SK, true, true>;
+    return pair == 2 ? (const void*)vat_stream<KV, D, 1, NS, 4, 2, SK, true, true>
+                     : (const void*)vat_stream<KV, D, 1, NS, 4, 1, SK, true, true>;
+  }
   if (rope) {
     // Queries rotated by RoPE at the row fetch: one row tile per wave.
     if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK, false, true>;

@@ -441,10 +441,13 @@ def test_rope_host_checks(lib):
     # The plain entry point passes no rows: a rope problem is refused there.
     assert _call(lib, prob) == 1
     for kw, code in [(dict(q_dtype=0, kv_dtype=0), 3), (dict(kv_dtype=2, head_dim=64), 3),
-                     (dict(has_mask=2, num_mask_bytes=100), 3), (dict(rope=2), 2)]:
+                     (dict(rope=2), 2)]:
         bad = base_problem(chunk_keys=0, rope=kw.pop("rope", 1), **kw)
         assert call(fake, bad) == code, kw
-    # Byte-row masks and fp32 caches plan normally without rope.
+    # Byte-row masks take RoPE (one row tile per wave); fp32 caches plan
+    # normally without it.
+    plan = B.vat_plan(base_problem(has_mask=2, num_mask_bytes=100, rope=1))
+    assert plan.kernel == 1 and plan.row_tiles_per_wave == 1
     assert B.vat_plan(base_problem(has_mask=2, num_mask_bytes=100)).kernel == 1
     plan = B.vat_plan(base_problem(rope=1, num_qo_heads=32, max_qo_len=64, num_qo_tokens=128))
     assert plan.row_tiles_per_wave == 1 and plan.rows_per_block <= 128

@@ -190,3 +190,43 @@ def test_write_then_attend_with_rope(gpu_lib, cid):
                            p.v_scale, k_cos_sin=cs)
     p.k_cache, p.v_cache = k2, v2
     compare(p, *to_f64(*got), *_oracle(p, cs), what=f"rope chain {cid}")
+
+
+# ---------------------------------------------------------------- RoPE with full byte-row masks
+
+
+@pytest.mark.parametrize("prefix", [4096, 32768])
+def test_query_rope_with_full_row_masks_on_the_tree_workload(gpu_lib, oracle_pool, prefix):
+    """The batch-1 tree workload with sglang's byte rows and rotated queries:
+    against the oracle, and bitwise equal to the packed-bit layout (RoPE keeps
+    one row tile per wave for both layouts, so the plans are the same)."""
+    p = make_config(3, prefix=prefix, mask_layout="rows")
+    q = make_config(3, prefix=prefix)
+    cs = rope_cos_sin(rope_positions(q), p.head_dim)
+    say(f"[rope rows config 3 prefix {prefix}]")
+    got = _rope_run(gpu_lib, p, cs)
+    compare(p, *to_f64(*got), *oracle_pool.run(p, q_cos_sin=cs), what=f"rope rows {prefix}")
+    bits = _rope_run(gpu_lib, q, cs)
+    assert torch.equal(got[0].view(torch.int16), bits[0].view(torch.int16))
+    assert torch.equal(got[1], bits[1])
+
+
+@pytest.mark.parametrize("seed", list(range(8)))
+def test_query_rope_with_full_row_masks_fuzz(gpu_lib, seed):
+    rng = np.random.default_rng(900 + seed)
+    kv_dt, D = [("bf16", 128), ("bf16", 64), ("e4m3", 128)][seed % 3]
+    B = int(rng.integers(1, 5))
+    G = int(rng.choice([1, 4, 8]))
+    lens = [int(x) for x in rng.integers(1, 40, size=B)]
+    p = make_case(seed, prefix_lens=[int(x) for x in rng.integers(0, 400, size=B)], qo_lens=lens,
+                  num_qo_heads=2 * G, num_kv_heads=2, head_dim=D,
+                  page_size=int(rng.choice([1, 4, 16, 64])), q_dtype="bf16", kv_dtype=kv_dt,
+                  mask_kind=["tree", "random", "chain", "full"][seed % 4],
+                  fp8_absmax_scales=(kv_dt == "e4m3"), mask_layout="rows",
+                  rows_prefix_fill=["ones", "zeros", "random"][seed % 3],
+                  rows_true_values=["ones", "random"][seed % 2])
+    cs = rope_cos_sin(rope_positions(p) + int(rng.integers(0, 100000)), D)
+    chunk = int(rng.choice([-1, 0, 64]))
+    say(f"[rope rows fuzz {seed}] {kv_dt} D={D} G={G} L={lens} chunk={chunk}")
+    got = _rope_run(gpu_lib, p, cs, chunk_keys=chunk)
+    compare(p, *to_f64(*got), *_oracle(p, cs), what=f"rope rows fuzz {seed}")
