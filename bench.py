@@ -422,6 +422,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph-stats", action="store_true",
                     help="skip the per-call graph-replay timings and the HBM read probe")
+    ap.add_argument("--oracle-workers", type=int, default=-1,
+                    help="oracle worker processes (-1: the host's cores, at most 16; 0: run the "
+                         "oracle in this process and start no process -- required under a "
+                         "profiler that initialises the GPU before the program starts)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run K device-to-device copies of MIB MiB (for scaling HBM "
                          "byte counters) and exit")
@@ -436,9 +440,10 @@ def main():
     # The oracle's worker processes start before this process touches the GPU.
     pool = None
     if not args.copy_calibration and args.op == "verify":
-        from tests.oracle_pool import OraclePool
+        from tests.oracle_pool import InProcessOracle, OraclePool
 
-        pool = OraclePool()
+        pool = InProcessOracle() if args.oracle_workers == 0 else OraclePool(
+            args.oracle_workers if args.oracle_workers > 0 else None)
     try:
         run_bench(args, pool)
     finally:
@@ -659,14 +664,16 @@ def run_bench(args, pool):
                                   "kernel": "vat_read_probe (16-byte non-temporal loads, "
                                             "8 workgroups per CU)"}
     if not args.no_cpu_baseline:
-        from tests.oracle_pool import cpu_model
+        from tests.oracle_pool import OraclePool, cpu_model
 
         line["cpu_baseline"] = {
             "value": round(tokens * cpu_reps / cpu_s, 3), "unit": "query-tokens/s",
             "cores": pool.workers, "kind": "oracle",
-            "sample": f"whole workload, {p.batch * p.num_kv_heads} (request, KV head) items over "
-                      f"{pool.workers} worker processes with one BLAS thread each, repeated "
-                      f"{cpu_reps}x, {cpu_s:.1f} s, NumPy float64; host CPU: {cpu_model()}"}
+            "sample": (f"whole workload, {p.batch * p.num_kv_heads} (request, KV head) items over "
+                       f"{pool.workers} worker processes with one BLAS thread each"
+                       if pool.workers > 1 or isinstance(pool, OraclePool) else
+                       "whole workload, in this process with one BLAS thread") +
+                      f", repeated {cpu_reps}x, {cpu_s:.1f} s, NumPy float64; host CPU: {cpu_model()}"}
     print(json.dumps(line), flush=True)
     if not verified:
         sys.exit(3)

@@ -154,3 +154,35 @@ class OraclePool:
             if time.perf_counter() - t0 >= min_seconds:
                 break
         return res, time.perf_counter() - t0, reps
+
+
+class InProcessOracle:
+    """The same interface without worker processes: the oracle runs in this
+    process with one BLAS thread. For runs where starting processes is not
+    allowed (a profiler that has initialised the GPU before the program
+    starts must not see this process fork and exec)."""
+
+    workers = 1
+
+    def close(self):
+        pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def run(self, p, requests: Optional[Sequence[int]] = None, q_cos_sin=None):
+        from threadpoolctl import threadpool_limits
+
+        from oracle import verify_attention as oracle_va
+
+        with threadpool_limits(1):
+            return oracle_va(p.q, p.k_cache, p.v_cache, p.kv_indptr, p.kv_indices, p.last_page_len,
+                             p.qo_indptr, p.mask, p.mask_indptr, sm_scale=p.sm_scale,
+                             k_scale=p.k_scale, v_scale=p.v_scale, q_dtype=p.q_dtype,
+                             kv_dtype=p.kv_dtype, requests=requests, mask_layout=p.mask_layout,
+                             q_cos_sin=q_cos_sin)
+
+    timed = OraclePool.timed
