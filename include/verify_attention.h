@@ -166,9 +166,9 @@ typedef struct {
                                row, for requests with many partials) or 16
                                (four rows per wave); 0 when direct */
   int32_t heads_per_group;  /* streaming kernel: KV heads one workgroup takes
-                               (1, or 2 adjacent heads read as one run per
-                               key: fp8 caches with D 128); grid_y counts
-                               head groups (times row blocks) */
+                               (1, or 2 or 4 adjacent heads read as one run
+                               per key: fp8 caches with D 128); grid_y
+                               counts head groups (times row blocks) */
 } vat_plan_t;
 
 /* Plan a call: validates the shapes and fills *plan. Host only; touches the

@@ -104,29 +104,35 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   const int64_t D = p->head_dim;
   const int64_t eb = elem_bytes(p->kv_dtype);
 
-  // Two KV heads per workgroup: fp8 caches with D = 128 (128-byte head
-  // rows) and an even head count, every head's rows in at most two tiles, a
-  // batch the balanced slices serve, no RoPE and no byte-row masks. A key's
-  // DMA then reads both heads' rows as one 256-byte run instead of two
-  // 128-byte runs 128 bytes apart, each fetched by another workgroup at
-  // another time. Computing waves: one tile each, the tiles of head h, then
-  // those of h + 1; four DMA waves; 64-key stages of 32 KB.
+  // Several KV heads per workgroup: fp8 caches with D = 128 (128-byte head
+  // rows) and a head count divisible by the group, every head's rows in at
+  // most two tiles, a batch the balanced slices serve, no RoPE and no
+  // byte-row masks. A key's DMA then reads the group's rows as one run (512
+  // bytes for four heads, 256 for two) instead of 128-byte runs, each
+  // fetched by another workgroup at another time.
+  //  * Four heads (head count divisible by 4): one computing wave per head
+  //    holding all of its row tiles, so each key and value is decoded once
+  //    per head; 32-key stages of 32 KB.
+  //  * Two heads: one tile per computing wave, the tiles of head h, then
+  //    those of h + 1; 64-key stages of 32 KB.
+  // Four DMA waves either way.
   const bool fp8 = p->kv_dtype == VAT_FP8_E4M3FN;
   if (fp8 && D == 128 && p->num_kv_heads % 2 == 0 && tiles <= 2 && !p->rope &&
       p->has_mask != 2 && p->chunk_keys == -1 && p->batch <= kSliceMaxBatch) {
     const int64_t M = tiles * 16;
-    const int64_t groups = p->num_kv_heads / 2;
+    const int64_t hp = p->num_kv_heads % 4 == 0 ? 4 : 2;
+    const int64_t groups = p->num_kv_heads / hp;
     plan->kernel = 1;
-    plan->heads_per_group = 2;
+    plan->heads_per_group = int32_t(hp);
     plan->threads = kStreamThreads;
-    plan->row_tiles_per_wave = 1;
-    plan->waves_rows = int32_t(2 * tiles);
+    plan->row_tiles_per_wave = hp == 4 ? int32_t(tiles) : 1;
+    plan->waves_rows = hp == 4 ? 4 : int32_t(2 * tiles);
     plan->waves_keys = 1;
     plan->dma_waves = 4;
     plan->rows_per_block = int32_t(M);
     plan->row_blocks = 1;
     plan->stages = 4;
-    plan->lds_bytes = 4 * 2 * 64 * 256 + kStreamPageWindow * 4;
+    plan->lds_bytes = 4 * 32 * 1024 + kStreamPageWindow * 4;
     int64_t nx = int64_t(num_cus) / groups;
     if (nx < 1) nx = 1;
     plan->slices = int32_t(nx);

@@ -37,8 +37,8 @@ constexpr int kSWaves = kStreamThreads / 64;  // 8
 
 // DW: waves issuing the DMA (2 or 4: the last ones of eight; 8: all of them);
 // SK: keys per stage.
-// HP: KV heads per workgroup (1, or 2 adjacent heads whose rows lie side by
-// side in each slot, so a key row in LDS is both heads' rows).
+// HP: KV heads per workgroup (1, or 2 or 4 adjacent heads whose rows lie
+// side by side in each slot, so a key row in LDS is all of their rows).
 template <int KV, int D, int DW = kSWaves, int SK = kStageKeys, int HP = 1>
 struct StreamGeom {
   static constexpr int EB = (KV == KV_E4M3) ? 1 : 2;  // bytes per cache element
@@ -56,26 +56,28 @@ struct StreamGeom {
 
 // LDS position of 16-byte chunk c of stage-local key kl: chunks are XOR
 // swizzled by the key so that the operand reads below (sixteen keys at one
-// chunk, or four keys at two chunks) fall in distinct banks.
+// chunk, or four keys at two chunks) fall in distinct banks. Rows of more
+// than sixteen chunks (several heads side by side) swizzle within aligned
+// groups of sixteen: that already spreads sixteen keys over every bank.
 template <int CPK>
-__device__ __forceinline__ int swz(int kl, int c) { return c ^ (kl & (CPK - 1)); }
+__device__ __forceinline__ int swz(int kl, int c) { return c ^ (kl & ((CPK < 16 ? CPK : 16) - 1)); }
 
 // Where compute_stage finds 16-byte chunk `ch` of key `kl`'s row (of the
 // wave's KV head) within a stage's K block, and where the V block starts.
 // Per-head stages (vat_stream) hold one KV head's rows, one after another,
 // chunks swizzled by swz().
-// With two heads per workgroup a key row holds both heads' rows; `hc` is
-// the wave's head's first chunk in it.
+// With several heads per workgroup a key row holds every one of their rows;
+// `hc` is the wave's head's first chunk in it.
 template <int KV, int D, int SK, int HP = 1>
 struct HeadLayout {
   static constexpr int ROW = StreamGeom<KV, D, kStreamThreads / 64, SK, HP>::ROW;
   static constexpr int CPK = ROW / 16;
   static constexpr int VBLK = SK * ROW;
   // Key kl + 16 m sits 16 m rows after key kl at the same swizzled chunk
-  // (the swizzle reads kl % CPK, CPK <= 16), so the per-lane part of an
-  // address is the same for every 16-key tile.
+  // (the swizzle reads at most kl % 16), so the per-lane part of an address
+  // is the same for every 16-key tile.
   static constexpr int KT_STRIDE = 16 * ROW;
-  static_assert(CPK <= 16, "tile-invariant swizzle");
+  static_assert(CPK <= 16 || CPK % 16 == 0, "tile-invariant swizzle");
   int hc = 0;
   __device__ __forceinline__ int off(int kl, int ch) const {
     return kl * ROW + (swz<CPK>(kl, hc + ch) << 4);
@@ -649,25 +651,26 @@ struct RowSet {
 // Write a finished segment's rows of this wave (`lrow`: the rows' full sums):
 // out (bf16) and natural-log lse for a whole request, otherwise a normalised
 // fp32 partial (v_scale not yet applied) and its base-2 log-sum-exp in slot
-// `slot`.
+// `slot`. The segment's rows are rbase .. rbase + 16 RT - 1 of the request's
+// G L rows (row r = t G + g).
 // `rb`: row block; `row0`: this wave's first row within the block.
-template <int KV, int D, int RT, bool ROWS, bool ROPE>
+template <int D, int RT>
 __device__ __forceinline__ void write_rows(const StreamAcc<D, RT>& acc, const float (&lrow)[RT],
-                                           const RowSet<KV, D, RT, ROWS, ROPE>& rs, const PartialArgs& a,
-                                           int q_start, bool whole, int slot, int rb, int row0,
-                                           int h, int lane) {
+                                           const PartialArgs& a, int q_start, int L, int rbase,
+                                           bool whole, int slot, int rb, int row0, int h, int lane) {
   constexpr int NDT = D / 16;
   const int l16 = lane & 15, j4 = lane >> 4;
   const long long pid = ((long long)slot * a.hkv + h) * a.row_blocks + rb;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const float lsum = lrow[rt];
-    if (!rs.row_ok[rt]) continue;
+    const int row = rbase + rt * 16 + l16;
+    if (row >= a.group * L) continue;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     const float lse2 = lsum > 0.f ? acc.m[rt] + fast_log2(lsum) : kNegInf;
     const int local = row0 + rt * 16 + l16;
     if (whole) {
-      const long long orow = (long long)(q_start + rs.row_t[rt]) * a.hq + h * a.group + rs.row_g[rt];
+      const long long orow = (long long)(q_start + row / a.group) * a.hq + h * a.group + row % a.group;
       unsigned short* op = (unsigned short*)a.out + orow * D;
       const float sc = inv * a.v_scale;
 #pragma unroll
@@ -758,9 +761,10 @@ __device__ __forceinline__ void merge_pair_state(StreamAcc<D, RT>& acc, float (&
 // through one ring of LDS buffers filled by DMA. Wave w < waves_rows owns row
 // tiles [w RT, w RT + RT) of every segment and runs all of its keys, so no
 // two waves ever hold parts of the same row; all eight waves issue the DMA.
-// HP = 2: the workgroup takes two adjacent KV heads, h and h + 1, whose rows
-// sit side by side in every slot, so each key's DMA reads one run of both
-// heads' rows; computing waves take the row tiles of h, then those of h + 1.
+// HP = 2 or 4: the workgroup takes HP adjacent KV heads, h .. h + HP - 1,
+// whose rows sit side by side in every slot, so each key's DMA reads one run
+// of all their rows; computing waves take the row tiles of h, then those of
+// h + 1, and so on.
 template <int KV, int D, int RT, int NS, int DW, int P, int SK, bool ROWS, bool ROPE, int HP = 1>
 __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   using G = StreamGeom<KV, D, DW, SK, HP>;
@@ -1010,8 +1014,8 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
         for (int rt = 0; rt < RT; ++rt) lrow[rt] = rowsum4_v(acc.l[rt]);
       }
       if (computes && has_rows && phase == 0)
-        write_rows<KV, D, RT, ROWS, ROPE>(acc, lrow, rs, a, lane_val(sg.q_start, s), lane_val(sg.whole, s) != 0,
-                              lane_val(sg.slot, s), lane_val(sg.rb, s), row0, hw, lane);
+        write_rows<D, RT>(acc, lrow, a, lane_val(sg.q_start, s), seg_L, rbase, lane_val(sg.whole, s) != 0,
+                          lane_val(sg.slot, s), lane_val(sg.rb, s), row0, hw, lane);
     }
   }
 }
@@ -1059,6 +1063,12 @@ const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int
   // one row tile per computing wave, four DMA waves.
   if (heads_per_group == 2)
     return (const void*)vat_stream<KV_E4M3, 128, 1, 4, 4, 1, 64, false, false, 2>;
+  // Four fp8 heads of D 128: 512-byte key rows, 32-key stages, one computing
+  // wave per head holding all of its row tiles (so each key and value is
+  // decoded once per head), four DMA waves.
+  if (heads_per_group == 4)
+    return rt == 2 ? (const void*)vat_stream<KV_E4M3, 128, 2, 4, 4, 1, 32, false, false, 4>
+                   : (const void*)vat_stream<KV_E4M3, 128, 1, 4, 4, 1, 32, false, false, 4>;
   static_assert(stream_stage_keys(KV_BF16, 128) == 64 && stream_stage_keys(KV_BF16, 64) == 128 &&
                 stream_stage_keys(KV_E4M3, 128) == 128, "stage sizes match the planner");
   const bool rows = mask_mode == 2, ro = rope != 0;

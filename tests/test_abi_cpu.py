@@ -109,11 +109,12 @@ def test_plans_for_the_workloads(lib, cid):
         assert plan.kernel == 1 and plan.rows_per_block == 256 and plan.row_blocks == 2
         assert plan.slices == 0 and plan.block_order == 1
     elif cid == 5:
-        # fp8 of D 128, 32 rows per KV head: two heads per workgroup, one row
-        # tile per computing wave (four), four DMA waves.
-        assert plan.kernel == 1 and plan.heads_per_group == 2 and plan.row_tiles_per_wave == 1
+        # fp8 of D 128, 32 rows per KV head, eight KV heads: four heads per
+        # workgroup, one computing wave per head with both row tiles, four
+        # DMA waves.
+        assert plan.kernel == 1 and plan.heads_per_group == 4 and plan.row_tiles_per_wave == 2
         assert plan.rows_per_block == 32 and plan.waves_rows == 4 and plan.dma_waves == 4
-        assert plan.slices == 64 and plan.grid_y == 4
+        assert plan.slices == 128 and plan.grid_y == 2
     else:
         assert plan.kernel == 1 and plan.threads == 512 and plan.slices > 0
     if not plan.direct:
@@ -309,23 +310,30 @@ def test_slice_segments_cover_each_request_once():
             assert merged[b] == [m[2] for m in mine]
 
 
-def test_two_heads_per_workgroup_only_where_the_shape_fits(lib):
+def test_head_groups_only_where_the_shape_fits(lib):
     """fp8 caches of D 128 with an even KV-head count, at most 32 rows per KV
-    head, planner-chosen slices, no RoPE, no byte-row masks: two heads per
-    workgroup; everything else one."""
+    head, planner-chosen slices, no RoPE, no byte-row masks: four heads per
+    workgroup when the head count is divisible by four (one computing wave a
+    head, holding all of its row tiles), else two (one row tile a wave);
+    everything else one."""
     fp8 = dict(kv_dtype=2, num_kv_heads=8, num_qo_heads=32, max_qo_len=8, num_qo_tokens=16)
-    assert B.vat_plan(base_problem(**fp8)).heads_per_group == 2
-    assert B.vat_plan(base_problem(**{**fp8, "num_kv_heads": 2, "num_qo_heads": 8})).heads_per_group == 2
+    plan = B.vat_plan(base_problem(**fp8))
+    assert plan.heads_per_group == 4 and plan.waves_rows == 4 and plan.row_tiles_per_wave == 2
+    assert plan.grid_y == 2 and plan.lds_bytes == 4 * 32 * 1024 + 2048 * 4
     plan = B.vat_plan(base_problem(**{**fp8, "max_qo_len": 4}))
-    assert plan.heads_per_group == 2 and plan.waves_rows == 2
-    assert B.vat_plan(base_problem(**{**fp8, "has_mask": 1, "num_mask_bytes": 16})).heads_per_group == 2
+    assert plan.heads_per_group == 4 and plan.waves_rows == 4 and plan.row_tiles_per_wave == 1
+    plan = B.vat_plan(base_problem(**{**fp8, "num_kv_heads": 2, "num_qo_heads": 8}))
+    assert plan.heads_per_group == 2 and plan.waves_rows == 4 and plan.row_tiles_per_wave == 1
+    plan = B.vat_plan(base_problem(**{**fp8, "num_kv_heads": 6, "num_qo_heads": 24, "max_qo_len": 4}))
+    assert plan.heads_per_group == 2 and plan.waves_rows == 2 and plan.grid_y == 3
+    assert B.vat_plan(base_problem(**{**fp8, "has_mask": 1, "num_mask_bytes": 16})).heads_per_group == 4
     for change in (dict(max_qo_len=9, num_qo_tokens=18), dict(num_kv_heads=1, num_qo_heads=4),
                    dict(num_kv_heads=3, num_qo_heads=12), dict(head_dim=64), dict(kv_dtype=1),
                    dict(rope=1), dict(chunk_keys=64), dict(has_mask=2, num_mask_bytes=64),
                    dict(batch=65, num_qo_tokens=65, max_qo_len=1, num_kv_indices=65)):
         assert B.vat_plan(base_problem(**{**fp8, **change})).heads_per_group == 1, change
-    plan = B.vat_plan(base_problem(**{**fp8, "num_cus": 4}))
-    assert plan.heads_per_group == 2 and plan.direct == 1 and plan.workspace_bytes == 0
+    plan = B.vat_plan(base_problem(**{**fp8, "num_cus": 2}))
+    assert plan.heads_per_group == 4 and plan.direct == 1 and plan.workspace_bytes == 0
 
 
 

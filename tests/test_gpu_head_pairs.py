@@ -1,14 +1,15 @@
-"""GPU parity of the two-heads-per-workgroup streaming kernel: fp8 e4m3
-caches of D 128 with an even number of KV heads, where one workgroup reads
-both heads' rows of every key as one 256-byte run.
+"""GPU parity of the streaming kernel with several KV heads per workgroup:
+fp8 e4m3 caches of D 128 where one workgroup reads the rows of two adjacent
+KV heads (256-byte runs per key) or, when the head count is divisible by
+four, of four (512-byte runs; twelve waves when each head has two row tiles).
 
-Against the oracle at the parity tolerances: query-head groups 1, 2 and 4
-(one or two row tiles per head), draft lengths up to 32 rows per head, every
-power-of-two page size from 1 to 256, causal, tree and random packed masks,
-requests without drafts, batches up to 64, slice counts from one (every
-request written directly) to more slices than pages, and slices longer than
-the page-id window. Bit-exact: a page-pool permutation, and a HIP graph
-replayed between eager calls.
+Against the oracle at the parity tolerances: both head groupings, query-head
+groups 1, 2 and 4 (one or two row tiles per head), draft lengths up to 32
+rows per head, every power-of-two page size from 1 to 256, causal, tree and
+random packed masks, requests without drafts, batches up to 64, slice counts
+from one (every request written directly) to more slices than pages, and
+slices longer than the page-id window. Bit-exact: a page-pool permutation,
+and a HIP graph replayed between eager calls.
 """
 
 import numpy as np
@@ -34,56 +35,67 @@ def _case(seed, B, G, Lmax, ps, mask_kind, prefix_hi=600, empty=False, kv="e4m3"
 
 
 CASES = [
-    # seed, batch, group, max L, page size, mask, num_cus
-    (1, 3, 4, 8, 16, "causal", 0),
-    (2, 5, 4, 8, 1, "tree", 0),
-    (3, 7, 2, 16, 4, "random", 0),
-    (4, 2, 1, 32, 64, "tree", 0),
-    (5, 4, 4, 8, 256, "causal", 0),
-    (6, 64, 4, 8, 16, "causal", 0),
-    (7, 6, 2, 5, 8, "chain", 0),
-    (8, 3, 4, 4, 2, "full", 0),
-    (9, 5, 4, 8, 16, "tree", 1),
-    (10, 5, 4, 8, 16, "tree", 3),
-    (11, 9, 1, 16, 32, "random", 7),
-    (12, 2, 4, 1, 16, "causal", 0),
-    (13, 12, 2, 8, 128, "tree", 40),
+    # seed, batch, group, max L, page size, mask, num_cus, KV heads
+    (1, 3, 4, 8, 16, "causal", 0, 8),
+    (2, 5, 4, 8, 1, "tree", 0, 8),
+    (3, 7, 2, 16, 4, "random", 0, 8),
+    (4, 2, 1, 32, 64, "tree", 0, 8),
+    (5, 4, 4, 8, 256, "causal", 0, 8),
+    (6, 64, 4, 8, 16, "causal", 0, 8),
+    (7, 6, 2, 5, 8, "chain", 0, 8),
+    (8, 3, 4, 4, 2, "full", 0, 8),
+    (9, 5, 4, 8, 16, "tree", 1, 8),
+    (10, 5, 4, 8, 16, "tree", 3, 8),
+    (11, 9, 1, 16, 32, "random", 7, 8),
+    (12, 2, 4, 1, 16, "causal", 0, 8),
+    (13, 12, 2, 8, 128, "tree", 40, 8),
+    (14, 64, 4, 8, 16, "causal", 0, 4),
+    (15, 5, 4, 8, 1, "tree", 0, 6),
+    (16, 7, 2, 16, 4, "random", 0, 2),
+    (17, 6, 4, 4, 16, "causal", 0, 6),
+    (18, 9, 1, 16, 32, "random", 5, 6),
+    (19, 40, 4, 8, 64, "tree", 0, 12),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"seed{c[0]}")
-def test_slot_row_kernel_matches_oracle(gpu_lib, case):
-    seed, B, G, Lmax, ps, mask, cus = case
-    p = _case(seed, B, G, Lmax, ps, mask, empty=seed % 2 == 0)
+def test_head_group_kernel_matches_oracle(gpu_lib, case):
+    seed, B, G, Lmax, ps, mask, cus, hkv = case
+    p = _case(seed, B, G, Lmax, ps, mask, empty=seed % 2 == 0, hkv=hkv)
     t = to_device(p)
     prob = gpu_lib.problem_from_tensors(t["q"], t["k_cache"], t["kv_indptr"], t["kv_indices"],
                                         t["mask"], p.max_qo_len, num_cus=cus)
     plan = gpu_lib.vat_plan(prob)
-    say(f"[slot rows seed {seed}] B={B} G={G} L<={Lmax} ps={ps} {mask} cus={cus or 'device'} "
-        f"slices={plan.slices} rt={plan.row_tiles_per_wave} direct={plan.direct}")
-    assert plan.kernel == 1 and plan.heads_per_group == 2
+    say(f"[head groups seed {seed}] B={B} Hkv={hkv} G={G} L<={Lmax} ps={ps} {mask} "
+        f"cus={cus or 'device'} heads/wg={plan.heads_per_group} threads={plan.threads} "
+        f"slices={plan.slices} direct={plan.direct}")
+    assert plan.kernel == 1 and plan.heads_per_group == (4 if hkv % 4 == 0 else 2)
     out, lse = run_gpu(gpu_lib, p, tensors=t, num_cus=cus)
-    compare(p, *to_f64(out, lse), *oracle_of(p), what=f"slot rows seed {seed}")
+    compare(p, *to_f64(out, lse), *oracle_of(p), what=f"head groups seed {seed}")
 
 
-def test_slot_row_slices_longer_than_the_page_window(gpu_lib, oracle_pool):
-    # Two slices (8 CUs over four head pairs) of about 2,600 pages each: more
-    # page ids than the 2,048-entry window, so each workgroup moves its window
-    # once.
-    p = make_case(21, prefix_lens=[41000, 42000], qo_lens=[8, 5], num_qo_heads=32,
-                  num_kv_heads=8, head_dim=128, page_size=16, kv_dtype="e4m3", mask_kind="tree",
+@pytest.mark.parametrize("hkv", [8, 6])
+def test_head_group_slices_longer_than_the_page_window(gpu_lib, oracle_pool, hkv):
+    # Two slices of about 2,600 pages each (CU count = 2 x head groups):
+    # more page ids than the 2,048-entry window, so each workgroup moves its
+    # window once.
+    hp = 4 if hkv % 4 == 0 else 2
+    cus = 2 * hkv // hp
+    p = make_case(21, prefix_lens=[41000, 42000], qo_lens=[8, 5], num_qo_heads=4 * hkv,
+                  num_kv_heads=hkv, head_dim=128, page_size=16, kv_dtype="e4m3", mask_kind="tree",
                   fp8_absmax_scales=True, max_qo_len=8)
     t = to_device(p)
     plan = gpu_lib.vat_plan(gpu_lib.problem_from_tensors(t["q"], t["k_cache"], t["kv_indptr"],
-                                                         t["kv_indices"], t["mask"], 8, num_cus=8))
-    say(f"[slot rows, window moves] pages={int(p.kv_indptr[-1])} slices={plan.slices}")
-    assert plan.heads_per_group == 2 and int(p.kv_indptr[-1]) / plan.slices > 2048
-    out, lse = run_gpu(gpu_lib, p, tensors=t, num_cus=8)
-    compare(p, *to_f64(out, lse), *oracle_pool.run(p), what="slot rows window moves")
+                                                         t["kv_indices"], t["mask"], 8, num_cus=cus))
+    say(f"[head groups, window moves] Hkv={hkv} pages={int(p.kv_indptr[-1])} slices={plan.slices}")
+    assert plan.heads_per_group == hp and int(p.kv_indptr[-1]) / plan.slices > 2048
+    out, lse = run_gpu(gpu_lib, p, tensors=t, num_cus=cus)
+    compare(p, *to_f64(out, lse), *oracle_pool.run(p), what=f"head groups window moves Hkv {hkv}")
 
 
-def test_slot_row_page_permutation_is_bitwise_invariant(gpu_lib):
-    p = _case(31, 6, 4, 8, 16, "tree")
+@pytest.mark.parametrize("hkv", [8, 6])
+def test_head_group_page_permutation_is_bitwise_invariant(gpu_lib, hkv):
+    p = _case(31, 6, 4, 8, 16, "tree", hkv=hkv)
     t = to_device(p)
     o0, l0 = run_gpu(gpu_lib, p, tensors=t)
     perm = np.random.default_rng(5).permutation(p.num_pages)
@@ -97,7 +109,7 @@ def test_slot_row_page_permutation_is_bitwise_invariant(gpu_lib):
     assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)) and torch.equal(l0, l1)
 
 
-def test_slot_row_graph_replay_is_bitwise_eager(gpu_lib):
+def test_head_group_graph_replay_is_bitwise_eager(gpu_lib):
     p = make_config(5)
     t = to_device(p)
     kw = dict(mask=t["mask"], mask_indptr=t["mask_indptr"], sm_scale=p.sm_scale,
