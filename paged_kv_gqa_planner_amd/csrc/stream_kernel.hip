@@ -223,7 +223,12 @@ __device__ __forceinline__ unsigned long long visible_bits(unsigned long long bi
 // stage.
 // QLO: the queries are carried as two bf16 terms (qf + qlo, a rotated query
 // that bf16 alone would round), and S^T takes one MFMA per term.
-template <int KV, int D, int RT, int KT, int SK, bool QLO, class LAY>
+// VT (bf16 caches): form each V^T read's address per key tile instead of
+// one base per d tile plus the tile's immediate offset. The latter takes
+// fewer integer ops per stage and is faster where two row tiles share the
+// reads; a lone computing wave that also issues DMA (decode) runs faster
+// with the former (its schedule keeps eight fewer base registers live).
+template <int KV, int D, int RT, int KT, int SK, bool QLO, class LAY, bool VT = false>
 __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsigned (&qf)[RT][D / 8],
                                               const unsigned (&qlo)[RT][QLO ? D / 8 : 1],
                                               const int (&row_t)[RT],
@@ -421,9 +426,9 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
     // reads complete in order).
     // Per-lane address of d tile dt in key tile 0; tile kt adds the
     // immediate kt KT_STRIDE.
+    const int klb = 4 * j4 + (l16 >> 2);
     unsigned vbase[NDT];
     {
-      const int klb = 4 * j4 + (l16 >> 2);
       const unsigned sb = (unsigned)(uintptr_t)(const lds_void_t*)stage + kt0 * LAY::KT_STRIDE;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
@@ -431,11 +436,20 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
         vbase[dt] = sb + lay.off(klb, d0 >> 3) + (d0 & 7) * 2;
       }
     }
+    // V^T read of key tile kt (of this wave's), d tile dt.
+    auto vread = [&]<int KTI>(int dt) {
+      if constexpr (VT) {
+        const int d0 = 16 * dt + 4 * (l16 & 3);
+        return lds_read_tr16(stage + LAY::VBLK + lay.off(16 * (kt0 + KTI) + klb, d0 >> 3) + (d0 & 7) * 2);
+      } else {
+        return lds_read_tr16_at<LAY::VBLK + KTI * LAY::KT_STRIDE>(vbase[dt]);
+      }
+    };
     constexpr bool kAhead = RT == 1;  // registers for a third tile of reads
     constexpr int NBUF = kAhead ? 2 : 1;
     s16x4 va[NBUF][NDT], vv[NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) va[0][dt] = lds_read_tr16_at<LAY::VBLK>(vbase[dt]);
+    for (int dt = 0; dt < NDT; ++dt) va[0][dt] = vread.template operator()<0>(dt);
     [&]<int... K>(std::integer_sequence<int, K...>) {
       (
           [&] {
@@ -443,11 +457,11 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
             constexpr bool ahead = kAhead && kb + 1 < NB;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
-              vv[dt] = lds_read_tr16_at<LAY::VBLK + (2 * kb + 1) * LAY::KT_STRIDE>(vbase[dt]);
+              vv[dt] = vread.template operator()<2 * kb + 1>(dt);
             if constexpr (ahead) {
 #pragma unroll
               for (int dt = 0; dt < NDT; ++dt)
-                va[(kb + 1) % NBUF][dt] = lds_read_tr16_at<LAY::VBLK + (2 * kb + 2) * LAY::KT_STRIDE>(vbase[dt]);
+                va[(kb + 1) % NBUF][dt] = vread.template operator()<2 * kb + 2>(dt);
             }
             [&]<int... I>(std::integer_sequence<int, I...>) {
               ((lds_wait_tied2<(ahead ? NDT : 0) + NDT - 1 - I>(va[kb % NBUF][I], vv[I]),
@@ -461,7 +475,7 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
             if constexpr (!kAhead && kb + 1 < NB) {
 #pragma unroll
               for (int dt = 0; dt < NDT; ++dt)
-                va[(kb + 1) % NBUF][dt] = lds_read_tr16_at<LAY::VBLK + (2 * kb + 2) * LAY::KT_STRIDE>(vbase[dt]);
+                va[(kb + 1) % NBUF][dt] = vread.template operator()<2 * kb + 2>(dt);
             }
           }(),
           ...);
@@ -998,9 +1012,10 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
     if (computes && has_rows) {
       const int n0 = lane_val(sg.lo, s) + (g - first) * SK;
       const unsigned char* stage = smem + (g % NS) * G::STAGE;
-      compute_stage<KV, D, RT, SK / 16 / P, SK, ROPE>(acc, rs.qf, rs.qlo, rs.row_t, rs.row_bits, vis,
-                                                      stage, n0, a.c_log2, lane, phase * (SK / 16 / P),
-                                                      HeadLayout<KV, D, SK, HP>{(hw - h) * (G::HROW / 16)});
+      compute_stage<KV, D, RT, SK / 16 / P, SK, ROPE, HeadLayout<KV, D, SK, HP>,
+                    DW == kSWaves && RT == 1 && P == 1>(acc, rs.qf, rs.qlo, rs.row_t, rs.row_bits, vis,
+                                                        stage, n0, a.c_log2, lane, phase * (SK / 16 / P),
+                                                        HeadLayout<KV, D, SK, HP>{(hw - h) * (G::HROW / 16)});
     }
     if (g == lane_val(sg.incl, s) - 1) {
       // The segment's last stage (every wave sees it).
