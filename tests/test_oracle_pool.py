@@ -1,12 +1,13 @@
 """The process pool that spreads the oracle over (request, KV head) items
 gives bitwise the result of one direct oracle call: every mask layout, fp8
-caches, RoPE rows, requests without query rows, page sizes 1 and 16."""
+caches, RoPE rows, requests without query rows, page sizes 1 and 16; and the
+in-process form gives the same bits."""
 
 import numpy as np
 import pytest
 
 from oracle import verify_attention as oracle_va
-from tests.oracle_pool import OraclePool, default_workers
+from tests.oracle_pool import InProcessOracle, OraclePool, default_workers
 from workloads import make_case, rope_cos_sin, rope_positions
 
 
@@ -55,3 +56,16 @@ def test_pool_restricted_to_some_requests(pool):
                      p.qo_indptr, None, None, sm_scale=p.sm_scale, q_dtype=p.q_dtype,
                      kv_dtype=p.kv_dtype, requests=[2])
     assert np.array_equal(o, want[0]) and np.array_equal(l, want[1])
+
+
+@pytest.mark.parametrize("name", ["tree_bits_fp8", "random_rows"])
+def test_in_process_form_equals_the_pool_bitwise(pool, name):
+    # The form the bench uses under a profiler (no worker processes).
+    p = make_case(19, **CASES[name])
+    cs = rope_cos_sin(rope_positions(p), p.head_dim)
+    want = pool.run(p, q_cos_sin=cs)
+    got = InProcessOracle().run(p, q_cos_sin=cs)
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+    got = InProcessOracle().run(p, requests=[1], q_cos_sin=cs)
+    want = pool.run(p, requests=[1], q_cos_sin=cs)
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
