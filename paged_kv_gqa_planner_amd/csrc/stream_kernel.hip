@@ -242,6 +242,20 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
   constexpr int NDT = D / 16;
   const int l16 = lane & 15;
   const int j4 = lane >> 4;
+  constexpr int NB = KT / 2;  // 32-key blocks
+  // fp8: the first 32-key block's V^T reads go out before the S^T products,
+  // so their latency hides under QK and the softmax.
+  unsigned vbase[NDT];
+  u32x2 raw[2][KV == KV_E4M3 ? NDT : 1];
+  if constexpr (KV == KV_E4M3) {
+    const int e = l16 >> 1;
+    const int klx = 16 * (e >> 2) + 4 * j4 + (e & 3);
+    const unsigned sb = (unsigned)(uintptr_t)(const lds_void_t*)stage + kt0 * LAY::KT_STRIDE;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) vbase[dt] = sb + lay.off(klx, dt) + 8 * (l16 & 1);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) raw[0][dt] = lds_read_tr8_at<LAY::VBLK>(vbase[dt]);
+  }
   // ---- S^T tiles: lane (key 16 kt + l % 16 as A row, query row l % 16 as
   // B column) accumulates over 32-wide d steps.
   f32x4 st[KT][RT];
@@ -370,7 +384,6 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
                                                    __builtin_bit_cast(bf16x8, u32x4{b0.x, b0.y, b1.x, b1.y}),
                                                    c, 0, 0, 0);
   };
-  constexpr int NB = KT / 2;  // 32-key blocks
   if constexpr (KV == KV_E4M3) {
     // One 8-bit transpose read per (32-key block, d tile): source lane s of
     // the 16-lane group j points at the 8 codes of k index 8 j + s / 2 at
@@ -379,17 +392,6 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
     // Block kb + 1's reads are in flight while block kb's MFMAs run.
     // Per-lane address of d tile dt in 32-key block 0; block kb adds the
     // immediate 2 kb KT_STRIDE.
-    unsigned vbase[NDT];
-    {
-      const int e = l16 >> 1;
-      const int klx = 16 * (e >> 2) + 4 * j4 + (e & 3);
-      const unsigned sb = (unsigned)(uintptr_t)(const lds_void_t*)stage + kt0 * LAY::KT_STRIDE;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) vbase[dt] = sb + lay.off(klx, dt) + 8 * (l16 & 1);
-    }
-    u32x2 raw[2][NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) raw[0][dt] = lds_read_tr8_at<LAY::VBLK>(vbase[dt]);
     [&]<int... K>(std::integer_sequence<int, K...>) {
       (
           [&] {
@@ -427,7 +429,6 @@ __device__ __forceinline__ void compute_stage(StreamAcc<D, RT>& acc, const unsig
     // Per-lane address of d tile dt in key tile 0; tile kt adds the
     // immediate kt KT_STRIDE.
     const int klb = 4 * j4 + (l16 >> 2);
-    unsigned vbase[NDT];
     {
       const unsigned sb = (unsigned)(uintptr_t)(const lds_void_t*)stage + kt0 * LAY::KT_STRIDE;
 #pragma unroll
