@@ -106,21 +106,23 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
 
   // Several KV heads per workgroup: fp8 caches with D = 128 (128-byte head
   // rows) and a head count divisible by the group, every head's rows in at
-  // most two tiles, a batch the balanced slices serve, no RoPE and no
-  // byte-row masks. A key's DMA then reads the group's rows as one run (512
-  // bytes for four heads, 256 for two) instead of 128-byte runs, each
-  // fetched by another workgroup at another time.
-  //  * Four heads (head count divisible by 4): one computing wave per head
-  //    holding all of its row tiles, so each key and value is decoded once
-  //    per head; 32-key stages of 32 KB.
-  //  * Two heads: one tile per computing wave, the tiles of head h, then
-  //    those of h + 1; 64-key stages of 32 KB.
+  // most two tiles, a batch the balanced slices serve and no byte-row masks.
+  // A key's DMA then reads the group's rows as one run (512 bytes for four
+  // heads, 256 for two) instead of 128-byte runs, each fetched by another
+  // workgroup at another time.
+  //  * Four heads (head count divisible by 4, no RoPE): one computing wave
+  //    per head holding all of its row tiles, so each key and value is
+  //    decoded once per head; 32-key stages of 32 KB.
+  //  * Two heads (other even head counts, and RoPE, whose rotated query
+  //    leaves the registers for one row tile per wave): one tile per
+  //    computing wave, the tiles of head h, then those of h + 1; 64-key
+  //    stages of 32 KB.
   // Four DMA waves either way.
   const bool fp8 = p->kv_dtype == VAT_FP8_E4M3FN;
-  if (fp8 && D == 128 && p->num_kv_heads % 2 == 0 && tiles <= 2 && !p->rope &&
-      p->has_mask != 2 && p->chunk_keys == -1 && p->batch <= kSliceMaxBatch) {
+  if (fp8 && D == 128 && p->num_kv_heads % 2 == 0 && tiles <= 2 && p->has_mask != 2 &&
+      p->chunk_keys == -1 && p->batch <= kSliceMaxBatch) {
     const int64_t M = tiles * 16;
-    const int64_t hp = p->num_kv_heads % 4 == 0 ? 4 : 2;
+    const int64_t hp = p->num_kv_heads % 4 == 0 && !p->rope ? 4 : 2;
     const int64_t groups = p->num_kv_heads / hp;
     plan->kernel = 1;
     plan->heads_per_group = int32_t(hp);

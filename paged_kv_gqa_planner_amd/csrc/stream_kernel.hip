@@ -1078,7 +1078,8 @@ const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int
   // Two fp8 heads of D 128 per workgroup: 256-byte key rows, 64-key stages,
   // one row tile per computing wave, four DMA waves.
   if (heads_per_group == 2)
-    return (const void*)vat_stream<KV_E4M3, 128, 1, 4, 4, 1, 64, false, false, 2>;
+    return rope ? (const void*)vat_stream<KV_E4M3, 128, 1, 4, 4, 1, 64, false, true, 2>
+                : (const void*)vat_stream<KV_E4M3, 128, 1, 4, 4, 1, 64, false, false, 2>;
   // Four fp8 heads of D 128: 512-byte key rows, 32-key stages, one computing
   // wave per head holding all of its row tiles (so each key and value is
   // decoded once per head), four DMA waves.

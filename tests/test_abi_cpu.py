@@ -312,10 +312,10 @@ def test_slice_segments_cover_each_request_once():
 
 def test_head_groups_only_where_the_shape_fits(lib):
     """fp8 caches of D 128 with an even KV-head count, at most 32 rows per KV
-    head, planner-chosen slices, no RoPE, no byte-row masks: four heads per
-    workgroup when the head count is divisible by four (one computing wave a
-    head, holding all of its row tiles), else two (one row tile a wave);
-    everything else one."""
+    head, planner-chosen slices, no byte-row masks: four heads per workgroup
+    when the head count is divisible by four and there is no RoPE (one
+    computing wave a head, holding all of its row tiles), else two (one row
+    tile a wave); everything else one."""
     fp8 = dict(kv_dtype=2, num_kv_heads=8, num_qo_heads=32, max_qo_len=8, num_qo_tokens=16)
     plan = B.vat_plan(base_problem(**fp8))
     assert plan.heads_per_group == 4 and plan.waves_rows == 4 and plan.row_tiles_per_wave == 2
@@ -327,9 +327,12 @@ def test_head_groups_only_where_the_shape_fits(lib):
     plan = B.vat_plan(base_problem(**{**fp8, "num_kv_heads": 6, "num_qo_heads": 24, "max_qo_len": 4}))
     assert plan.heads_per_group == 2 and plan.waves_rows == 2 and plan.grid_y == 3
     assert B.vat_plan(base_problem(**{**fp8, "has_mask": 1, "num_mask_bytes": 16})).heads_per_group == 4
+    # RoPE: two heads per workgroup, one row tile per wave.
+    plan = B.vat_plan(base_problem(**{**fp8, "rope": 1}))
+    assert plan.heads_per_group == 2 and plan.waves_rows == 4 and plan.row_tiles_per_wave == 1
     for change in (dict(max_qo_len=9, num_qo_tokens=18), dict(num_kv_heads=1, num_qo_heads=4),
                    dict(num_kv_heads=3, num_qo_heads=12), dict(head_dim=64), dict(kv_dtype=1),
-                   dict(rope=1), dict(chunk_keys=64), dict(has_mask=2, num_mask_bytes=64),
+                   dict(chunk_keys=64), dict(has_mask=2, num_mask_bytes=64),
                    dict(batch=65, num_qo_tokens=65, max_qo_len=1, num_kv_indices=65)):
         assert B.vat_plan(base_problem(**{**fp8, **change})).heads_per_group == 1, change
     plan = B.vat_plan(base_problem(**{**fp8, "num_cus": 2}))

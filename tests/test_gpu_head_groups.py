@@ -8,8 +8,9 @@ groups 1, 2 and 4 (one or two row tiles per head), draft lengths up to 32
 rows per head, every power-of-two page size from 1 to 256, causal, tree and
 random packed masks, requests without drafts, batches up to 64, slice counts
 from one (every request written directly) to more slices than pages, and
-slices longer than the page-id window. Bit-exact: a page-pool permutation,
-and a HIP graph replayed between eager calls.
+slices longer than the page-id window; with RoPE (two heads per workgroup,
+as RoPE plans take). Bit-exact: a page-pool permutation, and a HIP graph
+replayed between eager calls.
 """
 
 import numpy as np
@@ -17,7 +18,8 @@ import pytest
 import torch
 
 from tests.gpu_helpers import compare, oracle_of, run_gpu, say, to_device, to_f64
-from workloads import make_case, make_config
+from oracle import verify_attention as oracle_va
+from workloads import make_case, make_config, rope_cos_sin, rope_positions
 
 pytestmark = pytest.mark.gpu
 
@@ -140,3 +142,37 @@ def test_head_group_graph_replay_is_bitwise_eager(gpu_lib):
         assert torch.equal(lse, eager_l), rep
         eager_o, eager_l = gpu_lib.verify_attention(*args, **kw)
         torch.cuda.synchronize()
+
+
+ROPE_CASES = [
+    # seed, batch, group, max L, page size, mask, KV heads
+    (41, 5, 4, 8, 16, "tree", 8),
+    (42, 7, 2, 16, 4, "causal", 6),
+    (43, 12, 4, 8, 64, "random", 8),
+    (44, 3, 1, 32, 1, "chain", 4),
+]
+
+
+@pytest.mark.parametrize("case", ROPE_CASES, ids=lambda c: f"seed{c[0]}")
+def test_head_group_kernel_with_rope_matches_oracle(gpu_lib, case):
+    # RoPE plans take two heads per workgroup (one row tile per wave).
+    seed, B, G, Lmax, ps, mask, hkv = case
+    p = _case(seed, B, G, Lmax, ps, mask, hkv=hkv)
+    cs = rope_cos_sin(rope_positions(p), p.head_dim)
+    t = to_device(p)
+    prob = gpu_lib.problem_from_tensors(t["q"], t["k_cache"], t["kv_indptr"], t["kv_indices"],
+                                        t["mask"], p.max_qo_len, rope=True)
+    plan = gpu_lib.vat_plan(prob)
+    say(f"[head groups, rope seed {seed}] B={B} Hkv={hkv} G={G} L<={Lmax} ps={ps} {mask} "
+        f"heads/wg={plan.heads_per_group}")
+    assert plan.kernel == 1 and plan.heads_per_group == 2
+    out, lse = gpu_lib.verify_attention(
+        t["q"], t["k_cache"], t["v_cache"], t["kv_indptr"], t["kv_indices"], t["last_page_len"],
+        t["qo_indptr"], t["mask"], t["mask_indptr"], sm_scale=p.sm_scale, k_scale=p.k_scale,
+        v_scale=p.v_scale, max_qo_len=p.max_qo_len,
+        q_cos_sin=torch.from_numpy(np.ascontiguousarray(cs)).cuda())
+    torch.cuda.synchronize()
+    want = oracle_va(p.q, p.k_cache, p.v_cache, p.kv_indptr, p.kv_indices, p.last_page_len,
+                     p.qo_indptr, p.mask, p.mask_indptr, sm_scale=p.sm_scale, k_scale=p.k_scale,
+                     v_scale=p.v_scale, q_dtype=p.q_dtype, kv_dtype=p.kv_dtype, q_cos_sin=cs)
+    compare(p, *to_f64(out, lse), *want, what=f"head groups rope seed {seed}")
