@@ -1,14 +1,15 @@
 // Streaming partial kernel for verify shapes (bf16 or fp8 e4m3 caches, at
 // most 256 query rows per KV head).
 //
-// One workgroup (eight wave64s, two per SIMD) per (work item, KV head). It
-// holds all G * L_b query rows of the KV head (row r = t * G + g), so every
-// key and value is read from HBM once per KV head (flashmap page
-// "sglang/verify_attention.py", module docstring: all G query heads of a KV
-// head in one program). A work item is either a balanced slice of the
-// page-index space, holding the segments of the requests whose pages fall in
-// it, or one chunk of one request. Its keys stream through a ring of 64-key
-// LDS stages filled by gfx950's direct global->LDS 16-byte loads
+// One workgroup (eight wave64s, two per SIMD) per (work item, KV head), or
+// per (work item, group of two or four adjacent KV heads) for fp8 caches of
+// head size 128. It holds all G * L_b query rows of each of its KV heads
+// (row r = t * G + g), so every key and value is read from HBM once per KV
+// head (flashmap page "sglang/verify_attention.py", module docstring: all G
+// query heads of a KV head in one program). A work item is either a balanced
+// slice of the page-index space, holding the segments of the requests whose
+// pages fall in it, or one chunk of one request. Its keys stream through a
+// ring of 32 KB LDS stages filled by gfx950's direct global->LDS 16-byte loads
 // (global_load_lds_dwordx4), gathered page by page through the page table
 // (FlashInfer page "feat: Separate Q and KV dtypes for decode", paged layout);
 // the ring runs on across segment boundaries, so a slice pays the start-up
@@ -18,9 +19,11 @@
 // its softmax state never has to be combined with another wave's:
 //   S^T = K . Q^T      v_mfma_f32_16x16x32_bf16 (A = K from LDS, B = Q^T in VGPRs)
 //   online softmax     base 2, one running max per row, raised lazily
-//   O^T += V^T . P^T   v_mfma_f32_16x16x16_bf16 (A = V^T read with the LDS
-//                      transpose load ds_read_b64_tr_b16 for bf16 caches,
-//                      B = P^T: the exponentiated S^T tile, already in place)
+//   O^T += V^T . P^T   v_mfma_f32_16x16x32_bf16 over 32 keys, two 16-key
+//                      tiles side by side in k (A = V^T read with the LDS
+//                      transpose loads ds_read_b64_tr_b16 for bf16 caches or
+//                      ds_read_b64_tr_b8 for fp8, B = P^T: the exponentiated
+//                      S^T tiles, already in place)
 // fp8 keys and values are decoded to bf16 in registers (exactly) right after
 // the LDS reads. The draft block at the end of the request is masked in place:
 // draft j is visible to token t iff j <= t (causal) or mask bit (t, j) is set.
