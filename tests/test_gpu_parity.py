@@ -300,7 +300,7 @@ SLICE_CASES = {
 def test_balanced_slices_match_oracle(gpu_lib, name, num_cus):
     # The slice count follows the CU count the plan is made for, so these cover
     # one slice (direct), a few long slices spanning several requests, and more
-    # slices than keys (empty slices).
+    # slices than pages (empty slices).
     p = make_case(91, **SLICE_CASES[name])
     plan = gpu_lib.vat_plan(_problem(gpu_lib, p, num_cus=num_cus))
     say(f"[slices {name} num_cus={num_cus}] slices={plan.slices} direct={plan.direct}")
