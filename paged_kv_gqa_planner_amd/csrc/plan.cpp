@@ -221,13 +221,14 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   plan->row_blocks = int32_t(RB);
   if (int64_t(p->num_kv_heads) * RB > 65535) return VAT_ERR_UNSUPPORTED;
 
-  // LDS. Streaming: a ring of stages (K and V of 64 keys at bf16 D 128, else
-  // 128 keys), as many as fit the budget (2..8), plus the work item's page ids. Row-tiled: a
+  // LDS. Streaming: a ring of stages (K and V of 64 keys at bf16 D 128 with
+  // one row tile per wave, else 128 keys), as many as fit the budget (2..8),
+  // plus the work item's page ids. Row-tiled: a
   // per-wave 32-key V staging tile (bf16 after any fp8 decode) and the slots
   // of the key-splitting waves' combine.
   const int64_t ndt = D / 16;
   if (stream) {
-    const int64_t stage = 2 * int64_t(stream_stage_keys(p->kv_dtype, p->head_dim)) * D * eb;
+    const int64_t stage = 2 * int64_t(stream_stage_keys(p->kv_dtype, p->head_dim, rt)) * D * eb;
     int64_t ns = kStreamLdsBudget / stage;
     if (ns > 8) ns = 8;
     if (ns < 2) ns = 2;

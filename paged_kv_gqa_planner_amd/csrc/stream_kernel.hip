@@ -1016,10 +1016,20 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
     if (computes && has_rows) {
       const int n0 = lane_val(sg.lo, s) + (g - first) * SK;
       const unsigned char* stage = smem + (g % NS) * G::STAGE;
-      compute_stage<KV, D, RT, SK / 16 / P, SK, ROPE, HeadLayout<KV, D, SK, HP>,
-                    DW == kSWaves && RT == 1 && P == 1>(acc, rs.qf, rs.qlo, rs.row_t, rs.row_bits, vis,
-                                                        stage, n0, a.c_log2, lane, phase * (SK / 16 / P),
-                                                        HeadLayout<KV, D, SK, HP>{(hw - h) * (G::HROW / 16)});
+      // 128-key bf16 D = 128 stages are taken in two 64-key passes (the
+      // registers of one pass's scores); the second is skipped when the
+      // segment ends in the first. With one wave per tile set the first key
+      // tile of each pass is a constant, so its addresses fold into
+      // immediates.
+      constexpr int KP = (KV == KV_BF16 && D == 128 && SK == 128) ? 2 : 1;
+      constexpr int KTW = SK / 16 / P / KP;
+#pragma unroll
+      for (int kp = 0; kp < KP; ++kp) {
+        if (kp > 0 && n0 + kp * (SK / KP) >= vis.hi) break;
+        compute_stage<KV, D, RT, KTW, SK, ROPE, HeadLayout<KV, D, SK, HP>, DW == kSWaves && RT == 1 && P == 1>(
+            acc, rs.qf, rs.qlo, rs.row_t, rs.row_bits, vis, stage, n0, a.c_log2, lane,
+            (P == 1 ? 0 : phase * (SK / 16 / P)) + kp * KTW, HeadLayout<KV, D, SK, HP>{(hw - h) * (G::HROW / 16)});
+      }
     }
     if (g == lane_val(sg.incl, s) - 1) {
       // The segment's last stage (every wave sees it).
@@ -1069,7 +1079,11 @@ static const void* stream_variant(int rt, int dma_waves, int pair, bool rows, bo
                      : (const void*)vat_stream<KV, D, 1, NS, 4, 1, SK, true, false>;
   }
   if constexpr (KV != KV_E4M3)
-    if (rt == 2) return (const void*)vat_stream<KV, D, 2, NS, kSWaves, 1, SK, false, false>;
+    if (rt == 2) {
+      // bf16 D = 128: two 64 KB stages of 128 keys (the planner's choice).
+      if constexpr (D == 128) return (const void*)vat_stream<KV, D, 2, 2, kSWaves, 1, 2 * SK, false, false>;
+      else return (const void*)vat_stream<KV, D, 2, NS, kSWaves, 1, SK, false, false>;
+    }
   if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK, false, false>;
   if (dma_waves == 2) return (const void*)vat_stream<KV, D, 1, NS, 2, 1, SK, false, false>;
   return pair == 2 ? (const void*)vat_stream<KV, D, 1, NS, 4, 2, SK, false, false>
@@ -1090,7 +1104,8 @@ const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int
     return rt == 2 ? (const void*)vat_stream<KV_E4M3, 128, 2, 4, 4, 1, 32, false, false, 4>
                    : (const void*)vat_stream<KV_E4M3, 128, 1, 4, 4, 1, 32, false, false, 4>;
   static_assert(stream_stage_keys(KV_BF16, 128) == 64 && stream_stage_keys(KV_BF16, 64) == 128 &&
-                stream_stage_keys(KV_E4M3, 128) == 128, "stage sizes match the planner");
+                    stream_stage_keys(KV_E4M3, 128) == 128 && stream_stage_keys(KV_BF16, 128, 2) == 128,
+                "stage sizes match the planner");
   const bool rows = mask_mode == 2, ro = rope != 0;
   if (kv_dtype == KV_BF16)
     return head_dim == 128 ? stream_variant<KV_BF16, 128, 4, 64>(rt, dma_waves, pair, rows, ro)

@@ -104,10 +104,14 @@ def test_plans_for_the_workloads(lib, cid):
         # Prefill: the streaming kernel in row blocks of 256 rows, whole requests.
         assert plan.kernel == 1 and plan.direct == 1 and plan.workspace_bytes == 0
         assert plan.rows_per_block == 256 and plan.row_blocks == 32 and plan.slices == 0
+        # Two row tiles per wave: two 64 KB stages of 128 keys.
+        assert plan.row_tiles_per_wave == 2 and plan.stages == 2
+        assert plan.lds_bytes == 2 * 64 * 1024 + 2048 * 4
     elif cid == 7:
         # Wide trees: 512 rows per KV head in two blocks, chunked prefixes.
         assert plan.kernel == 1 and plan.rows_per_block == 256 and plan.row_blocks == 2
         assert plan.slices == 0 and plan.block_order == 1
+        assert plan.row_tiles_per_wave == 2 and plan.stages == 2
     elif cid == 5:
         # fp8 of D 128, 32 rows per KV head, eight KV heads: four heads per
         # workgroup, one computing wave per head with both row tiles, four
