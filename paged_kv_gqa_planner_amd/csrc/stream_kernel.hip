@@ -1018,17 +1018,24 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
       const unsigned char* stage = smem + (g % NS) * G::STAGE;
       // 128-key bf16 D = 128 stages are taken in two 64-key passes (the
       // registers of one pass's scores); the second is skipped when the
-      // segment ends in the first. With one wave per tile set the first key
-      // tile of each pass is a constant, so its addresses fold into
-      // immediates.
-      constexpr int KP = (KV == KV_BF16 && D == 128 && SK == 128) ? 2 : 1;
-      constexpr int KTW = SK / 16 / P / KP;
-#pragma unroll
-      for (int kp = 0; kp < KP; ++kp) {
-        if (kp > 0 && n0 + kp * (SK / KP) >= vis.hi) break;
-        compute_stage<KV, D, RT, KTW, SK, ROPE, HeadLayout<KV, D, SK, HP>, DW == kSWaves && RT == 1 && P == 1>(
-            acc, rs.qf, rs.qlo, rs.row_t, rs.row_bits, vis, stage, n0, a.c_log2, lane,
-            (P == 1 ? 0 : phase * (SK / 16 / P)) + kp * KTW, HeadLayout<KV, D, SK, HP>{(hw - h) * (G::HROW / 16)});
+      // segment ends in the first. There one wave owns each tile set, so the
+      // first key tile of each pass is a constant and its addresses fold
+      // into immediates.
+      constexpr bool kTwoPass = KV == KV_BF16 && D == 128 && SK == 128;
+      static_assert(!kTwoPass || P == 1, "two-pass stages take one wave per tile set");
+      using LAY = HeadLayout<KV, D, SK, HP>;
+      const LAY lay{(hw - h) * (G::HROW / 16)};
+      if constexpr (kTwoPass) {
+        constexpr int KTW = SK / 16 / P / 2;
+        compute_stage<KV, D, RT, KTW, SK, ROPE, LAY, false>(acc, rs.qf, rs.qlo, rs.row_t, rs.row_bits, vis,
+                                                             stage, n0, a.c_log2, lane, 0, lay);
+        if (n0 + SK / 2 < vis.hi)
+          compute_stage<KV, D, RT, KTW, SK, ROPE, LAY, false>(acc, rs.qf, rs.qlo, rs.row_t, rs.row_bits,
+                                                               vis, stage, n0, a.c_log2, lane, KTW, lay);
+      } else {
+        compute_stage<KV, D, RT, SK / 16 / P, SK, ROPE, LAY, DW == kSWaves && RT == 1 && P == 1>(
+            acc, rs.qf, rs.qlo, rs.row_t, rs.row_bits, vis, stage, n0, a.c_log2, lane, phase * (SK / 16 / P),
+            lay);
       }
     }
     if (g == lane_val(sg.incl, s) - 1) {
