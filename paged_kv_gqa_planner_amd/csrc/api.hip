@@ -14,7 +14,7 @@
 namespace vat {
 const void* tile_kernel(int kv_dtype, int head_dim, int rt);
 const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int pair,
-                          int mask_mode, int rope, int heads_per_group);
+                          int mask_mode, int rope, int heads_per_group, int stages);
 const void* merge_kernel(int q_is_f32, int head_dim, int rows_per_workgroup);
 const void* append_kernel(int src_dtype, int cache_dtype, int pow2_scales, int units);
 const void* append_rope_kernel(int src_dtype, int cache_dtype, int pow2_scales);
@@ -173,7 +173,7 @@ vat_status_t launch_partial(const vat_problem_t* p, const vat_plan_t& plan, cons
   const void* fn = plan.kernel == 1 ? vat::stream_kernel(p->kv_dtype, p->head_dim,
                                                           plan.row_tiles_per_wave, plan.dma_waves,
                                                           plan.waves_keys, p->has_mask, p->rope,
-                                                          plan.heads_per_group)
+                                                          plan.heads_per_group, plan.stages)
                                      : vat::tile_kernel(p->kv_dtype, p->head_dim,
                                                         plan.row_tiles_per_wave);
   if (plan.lds_bytes > 65536) {

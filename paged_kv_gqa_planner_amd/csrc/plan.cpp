@@ -228,7 +228,8 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
   // of the key-splitting waves' combine.
   const int64_t ndt = D / 16;
   if (stream) {
-    const int64_t stage = 2 * int64_t(stream_stage_keys(p->kv_dtype, p->head_dim, rt)) * D * eb;
+    const bool two_pass = stream_two_pass(p->kv_dtype, int(D), rt, dw, p->rope, p->has_mask, RB);
+    const int64_t stage = 2 * int64_t(two_pass ? 128 : stream_stage_keys(p->kv_dtype, p->head_dim)) * D * eb;
     int64_t ns = kStreamLdsBudget / stage;
     if (ns > 8) ns = 8;
     if (ns < 2) ns = 2;

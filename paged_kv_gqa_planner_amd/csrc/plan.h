@@ -19,12 +19,21 @@ constexpr int kStepKeys = 32;
 constexpr int kStreamThreads = 512;
 constexpr int kStageKeys = 64;
 // Keys per streaming stage: 64 when a key row is 256 bytes (bf16, D = 128),
-// else 128, so a stage is 32 KB either way -- except two row tiles per wave
-// of bf16 D = 128 (prefill blocks, wide trees): 128 keys, 64 KB stages, two
-// of them, each taken in two 64-key passes (half as many stage barriers; the
-// keys mostly come from L2, so one stage of look-ahead suffices).
-constexpr int stream_stage_keys(int kv_dtype, int head_dim, int row_tiles_per_wave = 1) {
-  return (kv_dtype == VAT_BF16 && head_dim == 128 && row_tiles_per_wave == 1) ? 64 : 128;
+// else 128, so a stage is 32 KB either way.
+constexpr int stream_stage_keys(int kv_dtype, int head_dim) {
+  return (kv_dtype == VAT_BF16 && head_dim == 128) ? 64 : 128;
+}
+// Two-pass stages: bf16 D = 128 plans with two row tiles per wave (prefill
+// blocks, wide trees), or with query RoPE, one tile per wave, all eight
+// waves issuing loads and several row blocks, stream 128-key stages (two of
+// 64 KB), each taken in two 64-key passes: half as many stage barriers. Their
+// keys come mostly from L2 (each group's row blocks share them), so one stage
+// of look-ahead suffices.
+constexpr bool stream_two_pass(int kv_dtype, int head_dim, int rt, int dma_waves, int rope,
+                               int mask_mode, long long row_blocks) {
+  return kv_dtype == VAT_BF16 && head_dim == 128 &&
+         (rt == 2 || (rope && rt == 1 && dma_waves == kStreamThreads / 64 && mask_mode != 2 &&
+                      row_blocks > 1));
 }
 constexpr int kStreamMaxTiles = 16;
 constexpr int kStreamLdsBudget = 128 * 1024;

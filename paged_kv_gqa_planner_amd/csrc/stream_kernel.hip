@@ -1027,11 +1027,12 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
       const LAY lay{(hw - h) * (G::HROW / 16)};
       if constexpr (kTwoPass) {
         constexpr int KTW = SK / 16 / P / 2;
-        compute_stage<KV, D, RT, KTW, SK, ROPE, LAY, false>(acc, rs.qf, rs.qlo, rs.row_t, rs.row_bits, vis,
-                                                             stage, n0, a.c_log2, lane, 0, lay);
+        constexpr bool VT = DW == kSWaves && RT == 1;  // one tile: V^T addresses per key tile
+        compute_stage<KV, D, RT, KTW, SK, ROPE, LAY, VT>(acc, rs.qf, rs.qlo, rs.row_t, rs.row_bits, vis,
+                                                          stage, n0, a.c_log2, lane, 0, lay);
         if (n0 + SK / 2 < vis.hi)
-          compute_stage<KV, D, RT, KTW, SK, ROPE, LAY, false>(acc, rs.qf, rs.qlo, rs.row_t, rs.row_bits,
-                                                               vis, stage, n0, a.c_log2, lane, KTW, lay);
+          compute_stage<KV, D, RT, KTW, SK, ROPE, LAY, VT>(acc, rs.qf, rs.qlo, rs.row_t, rs.row_bits,
+                                                            vis, stage, n0, a.c_log2, lane, KTW, lay);
       } else {
         compute_stage<KV, D, RT, SK / 16 / P, SK, ROPE, LAY, DW == kSWaves && RT == 1 && P == 1>(
             acc, rs.qf, rs.qlo, rs.row_t, rs.row_bits, vis, stage, n0, a.c_log2, lane, phase * (SK / 16 / P),
@@ -1063,7 +1064,7 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
 // 32 KB (64 bf16 keys of D = 128, else 128 keys); four of them fill the
 // 128 KB the planner gives the ring.
 template <int KV, int D, int NS, int SK>
-static const void* stream_variant(int rt, int dma_waves, int pair, bool rows, bool rope) {
+static const void* stream_variant(int rt, int dma_waves, int pair, bool rows, bool rope, bool two_pass) {
   if (rope && rows) {
     // RoPE with full byte-row masks: one row tile per wave.
     if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK, true, true>;
@@ -1073,7 +1074,13 @@ static const void* stream_variant(int rt, int dma_waves, int pair, bool rows, bo
   }
   if (rope) {
     // Queries rotated by RoPE at the row fetch: one row tile per wave.
-    if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK, false, true>;
+    if (dma_waves == kSWaves) {
+      // Several row blocks (the planner's two-pass stages): two 64 KB
+      // stages of 128 keys.
+      if constexpr (KV == KV_BF16 && D == 128)
+        if (two_pass) return (const void*)vat_stream<KV, D, 1, 2, kSWaves, 1, 2 * SK, false, true>;
+      return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK, false, true>;
+    }
     if (dma_waves == 2) return (const void*)vat_stream<KV, D, 1, NS, 2, 1, SK, false, true>;
     return pair == 2 ? (const void*)vat_stream<KV, D, 1, NS, 4, 2, SK, false, true>
                      : (const void*)vat_stream<KV, D, 1, NS, 4, 1, SK, false, true>;
@@ -1088,7 +1095,7 @@ static const void* stream_variant(int rt, int dma_waves, int pair, bool rows, bo
   if constexpr (KV != KV_E4M3)
     if (rt == 2) {
       // bf16 D = 128: two 64 KB stages of 128 keys (the planner's choice).
-      if constexpr (D == 128) return (const void*)vat_stream<KV, D, 2, 2, kSWaves, 1, 2 * SK, false, false>;
+      if constexpr (D == 128) return (const void*)vat_stream<KV, D, 2, 2, kSWaves, 1, 2 * SK, false, false>;  // two-pass
       else return (const void*)vat_stream<KV, D, 2, NS, kSWaves, 1, SK, false, false>;
     }
   if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK, false, false>;
@@ -1098,7 +1105,7 @@ static const void* stream_variant(int rt, int dma_waves, int pair, bool rows, bo
 }
 
 const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int pair,
-                          int mask_mode, int rope, int heads_per_group) {
+                          int mask_mode, int rope, int heads_per_group, int stages) {
   // Two fp8 heads of D 128 per workgroup: 256-byte key rows, 64-key stages,
   // one row tile per computing wave, four DMA waves.
   if (heads_per_group == 2)
@@ -1111,14 +1118,14 @@ const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int
     return rt == 2 ? (const void*)vat_stream<KV_E4M3, 128, 2, 4, 4, 1, 32, false, false, 4>
                    : (const void*)vat_stream<KV_E4M3, 128, 1, 4, 4, 1, 32, false, false, 4>;
   static_assert(stream_stage_keys(KV_BF16, 128) == 64 && stream_stage_keys(KV_BF16, 64) == 128 &&
-                    stream_stage_keys(KV_E4M3, 128) == 128 && stream_stage_keys(KV_BF16, 128, 2) == 128,
+                    stream_stage_keys(KV_E4M3, 128) == 128 && stream_two_pass(KV_BF16, 128, 2, 8, 0, 0, 1),
                 "stage sizes match the planner");
   const bool rows = mask_mode == 2, ro = rope != 0;
   if (kv_dtype == KV_BF16)
-    return head_dim == 128 ? stream_variant<KV_BF16, 128, 4, 64>(rt, dma_waves, pair, rows, ro)
-                           : stream_variant<KV_BF16, 64, 4, 128>(rt, dma_waves, pair, rows, ro);
+    return head_dim == 128 ? stream_variant<KV_BF16, 128, 4, 64>(rt, dma_waves, pair, rows, ro, stages == 2)
+                           : stream_variant<KV_BF16, 64, 4, 128>(rt, dma_waves, pair, rows, ro, false);
   // The planner keeps fp8 at one row tile per wave.
-  return stream_variant<KV_E4M3, 128, 4, 128>(1, dma_waves, pair, rows, ro);
+  return stream_variant<KV_E4M3, 128, 4, 128>(1, dma_waves, pair, rows, ro, false);
 }
 
 }  // namespace vat

@@ -314,6 +314,27 @@ def test_slice_segments_cover_each_request_once():
             assert merged[b] == [m[2] for m in mine]
 
 
+def test_two_pass_stages(lib):
+    """bf16 D 128 plans that read their keys mostly from L2 -- two row tiles
+    per wave, or query RoPE with one tile per wave, all eight waves issuing
+    and several row blocks -- stream 128-key stages, two of 64 KB; the rest
+    keep four 32 KB stages."""
+    def plan(cid, **kw):
+        return B.vat_plan(problem_of(make_config(cid), **kw))
+    for cid in (4, 7):
+        pl = plan(cid)
+        assert pl.row_tiles_per_wave == 2 and pl.stages == 2, cid
+        pl = plan(cid, rope=1)
+        assert pl.row_tiles_per_wave == 1 and pl.dma_waves == 8 and pl.row_blocks > 1, cid
+        assert pl.stages == 2 and pl.lds_bytes == 2 * 64 * 1024 + 2048 * 4, cid
+    for cid in (2, 3, 5, 6):
+        assert plan(cid).stages == 4 and plan(cid, rope=1).stages == 4, cid
+    # RoPE over eight row tiles in one row block (keys from HBM): four stages.
+    pl = B.vat_plan(base_problem(batch=1, num_qo_heads=32, num_kv_heads=8, max_qo_len=32,
+                                 num_qo_tokens=32, num_kv_indices=512, num_pages=512, rope=1))
+    assert pl.row_tiles_per_wave == 1 and pl.dma_waves == 8 and pl.row_blocks == 1 and pl.stages == 4
+
+
 def test_head_groups_only_where_the_shape_fits(lib):
     """fp8 caches of D 128 with an even KV-head count, at most 32 rows per KV
     head, planner-chosen slices, no byte-row masks: four heads per workgroup
