@@ -672,11 +672,16 @@ struct RowSet {
 // `slot`. The segment's rows are rbase .. rbase + 16 RT - 1 of the request's
 // G L rows (row r = t G + g).
 // `rb`: row block; `row0`: this wave's first row within the block.
-template <int D, int RT>
+// OPAQUE: the lane index passes through an empty asm first, so the
+// compiler cannot hoist the lane-dependent part of these addresses out of
+// the stage loop (where, in the two-tile two-pass variant, the hoisted
+// values would not fit the registers and spill).
+template <int D, int RT, bool OPAQUE = false>
 __device__ __forceinline__ void write_rows(const StreamAcc<D, RT>& acc, const float (&lrow)[RT],
                                            const PartialArgs& a, int q_start, int L, int rbase,
                                            bool whole, int slot, int rb, int row0, int h, int lane) {
   constexpr int NDT = D / 16;
+  if constexpr (OPAQUE) asm volatile("" : "+v"(lane));
   const int l16 = lane & 15, j4 = lane >> 4;
   const long long pid = ((long long)slot * a.hkv + h) * a.row_blocks + rb;
 #pragma unroll
@@ -1051,8 +1056,9 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
         for (int rt = 0; rt < RT; ++rt) lrow[rt] = rowsum4_v(acc.l[rt]);
       }
       if (computes && has_rows && phase == 0)
-        write_rows<D, RT>(acc, lrow, a, lane_val(sg.q_start, s), seg_L, rbase, lane_val(sg.whole, s) != 0,
-                          lane_val(sg.slot, s), lane_val(sg.rb, s), row0, hw, lane);
+        write_rows<D, RT, KV == KV_BF16 && D == 128 && SK == 128 && RT == 2>(
+            acc, lrow, a, lane_val(sg.q_start, s), seg_L, rbase, lane_val(sg.whole, s) != 0,
+            lane_val(sg.slot, s), lane_val(sg.rb, s), row0, hw, lane);
     }
   }
 }
