@@ -1068,7 +1068,10 @@ __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
 // last waves issue the loads, the first ones compute) or 8 (all issue); `pair`: 2 waves
 // per row tile set (each takes half of every stage's keys) or 1. Stages hold
 // 32 KB (64 bf16 keys of D = 128, else 128 keys); four of them fill the
-// 128 KB the planner gives the ring.
+// 128 KB the planner gives the ring -- except the planner's two-pass plans
+// for bf16 D = 128 (two row tiles per wave, or RoPE with eight issuing waves
+// and several row blocks; `two_pass`), whose ring holds two 64 KB stages of
+// 128 keys.
 template <int KV, int D, int NS, int SK>
 static const void* stream_variant(int rt, int dma_waves, int pair, bool rows, bool rope, bool two_pass) {
   if (rope && rows) {
@@ -1100,8 +1103,9 @@ static const void* stream_variant(int rt, int dma_waves, int pair, bool rows, bo
   }
   if constexpr (KV != KV_E4M3)
     if (rt == 2) {
-      // bf16 D = 128: two 64 KB stages of 128 keys (the planner's choice).
-      if constexpr (D == 128) return (const void*)vat_stream<KV, D, 2, 2, kSWaves, 1, 2 * SK, false, false>;  // two-pass
+      // bf16 D = 128: two 64 KB stages of 128 keys (the planner makes every
+      // two-tile plan of this shape two-pass).
+      if constexpr (D == 128) return (const void*)vat_stream<KV, D, 2, 2, kSWaves, 1, 2 * SK, false, false>;
       else return (const void*)vat_stream<KV, D, 2, NS, kSWaves, 1, SK, false, false>;
     }
   if (dma_waves == kSWaves) return (const void*)vat_stream<KV, D, 1, NS, kSWaves, 1, SK, false, false>;
