@@ -57,7 +57,8 @@
  * page_size for requests with pages; qo_indptr non-decreasing from 0 to T;
  * 0 <= L_b <= min(max_qo_len, kv_len_b); mask segments as above. Kernels
  * clamp every index they derive from these arrays, so a violation gives
- * unspecified values but never an out-of-bounds access.
+ * unspecified values but never an out-of-bounds access. vat_check_inputs
+ * checks the contract on the device and reports which rule a call breaks.
  *
  * Calls never allocate, free, synchronise or read device memory on the
  * host. They enqueue at most two kernels on `stream` (a hipStream_t; NULL =
@@ -126,8 +127,13 @@ typedef struct {
                                with D 128; rows in blocks of up to 256 (bf16) or
                                128 (fp8, or full byte-row masks) per KV head);
                                0: row-tiled kernel (fp32 KV, fp8 KV with D 64) */
-  int32_t stages;           /* streaming kernel: 32 KB stages in flight in LDS
-                               (64 keys at bf16 D 128, else 128 keys) */
+  int32_t stages;           /* streaming kernel: stages in the LDS ring. 32 KB
+                               stages (64 keys at bf16 D 128, else 128 keys),
+                               or, for bf16 D 128 plans whose waves hold two
+                               row tiles (and query-RoPE plans of one tile
+                               per wave, all eight waves loading and several
+                               row blocks), two 64 KB stages of 128 keys
+                               each, computed in two 64-key passes */
   int32_t slices;           /* > 0: balanced scheduling. Per KV head, the page-index
                                space [0, num_kv_indices) is cut into `slices` equal
                                ranges, one workgroup each, which processes the
@@ -323,6 +329,34 @@ vat_status_t vat_append_kv_rope(const vat_problem_t* problem, int32_t src_dtype,
                                 const int32_t* kv_indices, const int32_t* last_page_len,
                                 const int32_t* qo_indptr, const float* k_cos_sin, float k_scale,
                                 float v_scale, void* stream);
+
+/* Status bits of vat_check_inputs: which rule of the device-content contract
+ * the arrays break (several may be set). */
+#define VAT_CHECK_KV_INDPTR 1   /* kv_indptr[0] != 0, decreasing, or > num_kv_indices */
+#define VAT_CHECK_KV_INDICES 2  /* a used page id outside [0, num_pages) */
+#define VAT_CHECK_LAST_PAGE 4   /* last_page_len outside [1, page_size] (requests with pages) */
+#define VAT_CHECK_QO_INDPTR 8   /* qo_indptr[0] != 0, decreasing, > T, or qo_indptr[B] != T */
+#define VAT_CHECK_QO_LEN 16     /* L_b > max_qo_len or L_b > kv_len_b */
+#define VAT_CHECK_MASK 32       /* a mask segment negative or past num_mask_bytes */
+
+/* Debugging aid, not a step of the path: check the device-content contract
+ * stated at the top of this header for the index arrays and mask offsets of
+ * a call, and write to *status (device int32, caller-owned) the OR of the
+ * VAT_CHECK_* bits of the rules they break, 0 when they keep all of them.
+ * The paged-format rules are the FlashInfer page "feat: Separate Q and KV
+ * dtypes for decode" (begin_forward docstring); the query and mask rules
+ * are this header's layouts. Arguments as verify_attention (mask_indptr is
+ * read only when has_mask; kv_indices only up to kv_indptr[B], cut to
+ * num_kv_indices); every read stays inside the sizes *problem declares,
+ * whatever the arrays hold. Enqueues two kernels on `stream` (clear, then
+ * check), allocates nothing and is capturable; read *status after the
+ * stream has reached them. Host errors (VAT_ERR_NULL, VAT_ERR_ALIGN for
+ * int32 arrays not 4-byte aligned, and those of vat_plan's shape checks)
+ * return before anything is enqueued. */
+vat_status_t vat_check_inputs(const vat_problem_t* problem, const int32_t* kv_indptr,
+                              const int32_t* kv_indices, const int32_t* last_page_len,
+                              const int32_t* qo_indptr, const int32_t* mask_indptr,
+                              int32_t* status, void* stream);
 
 /* Measurement aid, not a step of the path: read `bytes` of device memory at
  * `buf` once, start to end, with 16-byte non-temporal loads spread over

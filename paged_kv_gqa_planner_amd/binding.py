@@ -91,6 +91,8 @@ def load(path: Optional[str] = None):
     lib.vat_append_kv.restype = ctypes.c_int
     lib.verify_attention_noalloc.argtypes = full[:15] + [vp]
     lib.verify_attention_noalloc.restype = ctypes.c_int
+    lib.vat_check_inputs.argtypes = [P(VatProblem), vp, vp, vp, vp, vp, vp, vp]
+    lib.vat_check_inputs.restype = ctypes.c_int
     lib.vat_read_probe.argtypes = [vp, ctypes.c_size_t, vp, vp]
     lib.vat_read_probe.restype = ctypes.c_int
     lib.vat_status_string.argtypes = [ctypes.c_int]
@@ -443,6 +445,46 @@ class PreparedCall:
 
     def merge(self):
         _check(self.lib.vat_launch_merge(*self.merge_args), "vat_launch_merge")
+
+
+CHECK_BITS = {1: "kv_indptr", 2: "kv_indices", 4: "last_page_len", 8: "qo_indptr", 16: "qo_len",
+              32: "mask"}
+
+
+def check_inputs(q, k_cache, kv_indptr, kv_indices, last_page_len, qo_indptr, mask=None,
+                 mask_indptr=None, max_qo_len=None, mask_layout="bits", status=None,
+                 stream=None) -> int:
+    """Check the device-content contract of a call's index arrays and mask
+    offsets on the device (a debugging aid) and return the OR of the
+    VAT_CHECK_* bits of the rules they break (0: none; ``CHECK_BITS`` names
+    each bit). Shapes come from the tensors as in ``verify_attention``;
+    ``status`` is an optional one-element int32 device tensor to write into.
+    Synchronises the stream to read the result."""
+    import torch
+
+    idx = [("kv_indptr", kv_indptr), ("kv_indices", kv_indices), ("last_page_len", last_page_len),
+           ("qo_indptr", qo_indptr), ("mask_indptr", mask_indptr)]
+    for name, t in idx:
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.int32:
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    batch = kv_indptr.numel() - 1
+    if qo_indptr.numel() != batch + 1 or last_page_len.numel() != batch:
+        raise ValueError("qo_indptr must have batch + 1 entries and last_page_len batch")
+    if mask is not None and (mask_indptr is None or mask_indptr.numel() < batch):
+        raise ValueError("a mask needs mask_indptr with an offset per request")
+    problem = problem_from_tensors(q, k_cache, kv_indptr, kv_indices, mask, max_qo_len,
+                                   num_cus=1, mask_layout=mask_layout)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=kv_indptr.device)
+    lib = load()
+    _check(lib.vat_check_inputs(ctypes.byref(problem), _ptr(kv_indptr), _ptr(kv_indices),
+                                _ptr(last_page_len), _ptr(qo_indptr), _ptr(mask_indptr),
+                                _ptr(status), _stream_handle(stream)), "vat_check_inputs")
+    s = stream if stream is not None else torch.cuda.current_stream()
+    s.synchronize()
+    return int(status.item())
 
 
 def read_probe(buf, sink, stream=None):

@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libvat.so")
 ARCH = "gfx950"
 
 SOURCES = ["plan.cpp", "tile_kernel.hip", "stream_kernel.hip", "merge_kernel.hip", "append_kernel.hip",
-           "probe_kernel.hip", "api.hip"]
+           "probe_kernel.hip", "check_kernel.hip", "api.hip"]
 
 
 def hipcc() -> str:

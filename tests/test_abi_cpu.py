@@ -582,6 +582,27 @@ def test_read_probe_host_checks(lib):
     assert lib.vat_read_probe(vp(4096), 64, vp(8194), None) == 4   # sink misaligned
 
 
+def test_check_inputs_host_checks(lib):
+    """The device-content check rejects missing or misaligned arrays and
+    invalid shapes before anything is enqueued."""
+    vp = ctypes.c_void_p
+    prob = base_problem(chunk_keys=0)
+    a = [vp(0x1000), vp(0x2000), vp(0x3000), vp(0x4000), None, vp(0x5000)]
+    assert lib.vat_check_inputs(None, *a, None) == 1
+    assert lib.vat_check_inputs(ctypes.byref(prob), *a[:5], None, None) == 1      # status
+    assert lib.vat_check_inputs(ctypes.byref(prob), None, *a[1:], None) == 1      # kv_indptr
+    assert lib.vat_check_inputs(ctypes.byref(prob), a[0], None, *a[2:], None) == 1
+    assert lib.vat_check_inputs(ctypes.byref(prob), *a[:2], None, *a[3:], None) == 1
+    assert lib.vat_check_inputs(ctypes.byref(prob), *a[:3], None, *a[4:], None) == 1
+    assert lib.vat_check_inputs(ctypes.byref(prob), *a[:5], vp(0x5002), None) == 4
+    assert lib.vat_check_inputs(ctypes.byref(prob), vp(0x1001), *a[1:], None) == 4
+    masked = base_problem(chunk_keys=0, has_mask=1, num_mask_bytes=8)
+    assert lib.vat_check_inputs(ctypes.byref(masked), *a, None) == 1              # mask_indptr
+    assert lib.vat_check_inputs(ctypes.byref(masked), *a[:4], vp(0x6002), a[5], None) == 4
+    bad = base_problem(chunk_keys=0, num_kv_heads=3)                                # Hq % Hkv
+    assert lib.vat_check_inputs(ctypes.byref(bad), *a, None) == 2
+
+
 def test_noalloc_refuses_an_oversized_workspace_on_the_host(lib):
     """verify_attention_noalloc checks the planned workspace against its static
     array before anything else touches the device."""
