@@ -264,3 +264,58 @@ def test_random_corruptions_match_the_host_walk(gpu_lib):
         seen |= want
         assert got == want, (case, want, got)
     assert seen == KV_INDPTR | KV_INDICES | LAST_PAGE | QO_INDPTR | QO_LEN | MASK
+
+
+def test_check_in_a_hip_graph(gpu_lib):
+    """The clear and check kernels capture into a graph: replays after the
+    arrays change in place report the new contents, a replay after a failing
+    one starts from a cleared word, and eager calls run between replays."""
+    import ctypes
+
+    a = Arrays.of_problem(valid("ragged_bits"))
+    used = int(a.kv_indptr[-1])
+    dev = {k: torch.from_numpy(np.ascontiguousarray(getattr(a, k))).cuda()
+           for k in ("kv_indptr", "kv_indices", "last_page_len", "qo_indptr", "mask_indptr")}
+    status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    problem = B.make_problem(batch=len(a.kv_indptr) - 1, num_qo_heads=a.hq, num_kv_heads=a.hkv,
+                             head_dim=a.d, page_size=a.page_size, num_pages=a.num_pages,
+                             num_kv_indices=a.kv_indices.size, num_qo_tokens=a.tokens,
+                             max_qo_len=a.max_qo_len, q_dtype=B.VAT_BF16, kv_dtype=B.VAT_BF16,
+                             has_mask=1, num_mask_bytes=a.num_mask_bytes, num_cus=1)
+    lib = B.load()
+
+    def enqueue():
+        st = lib.vat_check_inputs(ctypes.byref(problem), dev["kv_indptr"].data_ptr(),
+                                  dev["kv_indices"].data_ptr(), dev["last_page_len"].data_ptr(),
+                                  dev["qo_indptr"].data_ptr(), dev["mask_indptr"].data_ptr(),
+                                  status.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        enqueue()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        enqueue()
+    steps = [
+        (lambda: dev["kv_indices"].__setitem__(used - 1, a.num_pages), KV_INDICES),
+        (lambda: dev["kv_indices"].__setitem__(used - 1, int(a.kv_indices[used - 1])), 0),
+        (lambda: dev["last_page_len"].__setitem__(1, 0), LAST_PAGE),
+        (lambda: dev["mask_indptr"].__setitem__(2, -4), LAST_PAGE | MASK),
+        (lambda: (dev["last_page_len"].__setitem__(1, int(a.last_page_len[1])),
+                  dev["mask_indptr"].__setitem__(2, int(a.mask_indptr[2]))), 0),
+    ]
+    for rep, (change, want) in enumerate(steps):
+        change()
+        status.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        got = int(status.item())
+        say(f"[check graph replay {rep}] want={want} got={got}")
+        assert got == want
+        # Eager work between replays: a check of the unchanged valid arrays.
+        assert Arrays.of_problem(valid("ragged_bits")).run() == 0
