@@ -245,7 +245,7 @@ def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, 
                      k_scale: float = 1.0, v_scale: float = 1.0, max_qo_len: Optional[int] = None,
                      out=None, lse=None, workspace=None, chunk_keys: int = -1, num_cus: int = 0,
                      stream=None, mask_layout: str = "bits",
-                     q_cos_sin=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+                     q_cos_sin=None, check: bool = False) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """Multi-query verification attention over a paged KV cache; returns (out, lse).
 
     ``sm_scale`` defaults to ``head_dim ** -0.5``; ``max_qo_len`` (the largest
@@ -256,11 +256,20 @@ def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, 
     ``mask_layout``: "bits" (packed L x L blocks) or "rows" (sglang's full
     byte rows). ``q_cos_sin`` ([T, D] float32 cos/sin rows of the query
     tokens' positions) rotates the queries by RoPE inside the kernel.
+    ``check`` (a debugging aid) first runs the device-content check
+    (``vat_check_inputs``) on the same stream, waits for it and raises
+    ``VatContentError`` naming the broken rules before anything else is
+    enqueued.
     """
     lib = load()
     problem, sm, out, lse, workspace, ws_bytes = _prepare(
         q, k_cache, v_cache, kv_indptr, kv_indices, last_page_len, qo_indptr, mask, mask_indptr,
         sm_scale, max_qo_len, out, lse, workspace, chunk_keys, num_cus, mask_layout, q_cos_sin)
+    if check:
+        bits = _run_check(problem, kv_indptr, kv_indices, last_page_len, qo_indptr, mask,
+                          mask_indptr, None, stream)
+        if bits:
+            raise VatContentError(bits)
     head = (ctypes.byref(problem), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_indptr),
             _ptr(kv_indices), _ptr(last_page_len), _ptr(qo_indptr), _ptr(mask), _ptr(mask_indptr))
     tail = (sm, float(k_scale), float(v_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
@@ -451,15 +460,17 @@ CHECK_BITS = {1: "kv_indptr", 2: "kv_indices", 4: "last_page_len", 8: "qo_indptr
               32: "mask"}
 
 
-def check_inputs(q, k_cache, kv_indptr, kv_indices, last_page_len, qo_indptr, mask=None,
-                 mask_indptr=None, max_qo_len=None, mask_layout="bits", status=None,
-                 stream=None) -> int:
-    """Check the device-content contract of a call's index arrays and mask
-    offsets on the device (a debugging aid) and return the OR of the
-    VAT_CHECK_* bits of the rules they break (0: none; ``CHECK_BITS`` names
-    each bit). Shapes come from the tensors as in ``verify_attention``;
-    ``status`` is an optional one-element int32 device tensor to write into.
-    Synchronises the stream to read the result."""
+class VatContentError(ValueError):
+    """Device contents break the contract; ``bits`` is the VAT_CHECK_* OR."""
+
+    def __init__(self, bits: int):
+        self.bits = bits
+        names = [n for b, n in CHECK_BITS.items() if bits & b]
+        super().__init__(f"device contents break the contract: {', '.join(names)} (bits {bits})")
+
+
+def _run_check(problem, kv_indptr, kv_indices, last_page_len, qo_indptr, mask, mask_indptr,
+               status, stream) -> int:
     import torch
 
     idx = [("kv_indptr", kv_indptr), ("kv_indices", kv_indices), ("last_page_len", last_page_len),
@@ -474,8 +485,6 @@ def check_inputs(q, k_cache, kv_indptr, kv_indices, last_page_len, qo_indptr, ma
         raise ValueError("qo_indptr must have batch + 1 entries and last_page_len batch")
     if mask is not None and (mask_indptr is None or mask_indptr.numel() < batch):
         raise ValueError("a mask needs mask_indptr with an offset per request")
-    problem = problem_from_tensors(q, k_cache, kv_indptr, kv_indices, mask, max_qo_len,
-                                   num_cus=1, mask_layout=mask_layout)
     if status is None:
         status = torch.empty(1, dtype=torch.int32, device=kv_indptr.device)
     lib = load()
@@ -485,6 +494,21 @@ def check_inputs(q, k_cache, kv_indptr, kv_indices, last_page_len, qo_indptr, ma
     s = stream if stream is not None else torch.cuda.current_stream()
     s.synchronize()
     return int(status.item())
+
+
+def check_inputs(q, k_cache, kv_indptr, kv_indices, last_page_len, qo_indptr, mask=None,
+                 mask_indptr=None, max_qo_len=None, mask_layout="bits", status=None,
+                 stream=None) -> int:
+    """Check the device-content contract of a call's index arrays and mask
+    offsets on the device (a debugging aid) and return the OR of the
+    VAT_CHECK_* bits of the rules they break (0: none; ``CHECK_BITS`` names
+    each bit). Shapes come from the tensors as in ``verify_attention``;
+    ``status`` is an optional one-element int32 device tensor to write into.
+    Synchronises the stream to read the result."""
+    problem = problem_from_tensors(q, k_cache, kv_indptr, kv_indices, mask, max_qo_len,
+                                   num_cus=1, mask_layout=mask_layout)
+    return _run_check(problem, kv_indptr, kv_indices, last_page_len, qo_indptr, mask, mask_indptr,
+                      status, stream)
 
 
 def read_probe(buf, sink, stream=None):

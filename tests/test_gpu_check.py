@@ -319,3 +319,29 @@ def test_check_in_a_hip_graph(gpu_lib):
         assert got == want
         # Eager work between replays: a check of the unchanged valid arrays.
         assert Arrays.of_problem(valid("ragged_bits")).run() == 0
+
+
+def test_verify_attention_check_option(gpu_lib):
+    """verify_attention(check=True): valid arrays give bitwise the plain
+    call's result; a page id out of range raises VatContentError with its bit
+    before the attention kernels are enqueued (out keeps its contents)."""
+    p = valid("ragged_bits")
+    t = to_device(p)
+    kw = dict(mask=t["mask"], mask_indptr=t["mask_indptr"], sm_scale=p.sm_scale,
+              max_qo_len=p.max_qo_len)
+    args = lambda tt: (tt["q"], tt["k_cache"], tt["v_cache"], tt["kv_indptr"], tt["kv_indices"],
+                       tt["last_page_len"], tt["qo_indptr"])
+    o0, l0 = B.verify_attention(*args(t), **kw)
+    o1, l1 = B.verify_attention(*args(t), check=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)) and torch.equal(l0, l1)
+    bad = dict(t)
+    bad["kv_indices"] = t["kv_indices"].clone()
+    bad["kv_indices"][int(p.kv_indptr[-1]) - 1] = p.num_pages
+    out = torch.full_like(t["q"], 7.0)
+    with pytest.raises(B.VatContentError) as err:
+        B.verify_attention(*args(bad), check=True, out=out, **kw)
+    say(f"[check option] {err.value}")
+    assert err.value.bits == KV_INDICES
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
