@@ -26,10 +26,15 @@ MAX_WORK = 6e8
 MAX_CACHE = 3e7
 
 
-def _fuzz_case(seed):
-    rng = np.random.default_rng(5000 + seed)
+def _dtypes(seed, rng):
     q_dt, kv_dt = [("bf16", "bf16"), ("bf16", "e4m3"), ("bf16", "e4m3"), ("f32", "f32")][seed % 4]
     D = 128 if kv_dt == "e4m3" and seed % 3 else int(rng.choice([64, 128]))
+    return q_dt, kv_dt, D
+
+
+def _fuzz_case(seed):
+    rng = np.random.default_rng(5000 + seed)
+    q_dt, kv_dt, D = _dtypes(seed, rng)
     hkv = int(rng.choice([2, 4, 8, 12]))
     G = int(rng.choice([1, 2, 4, 8, 16]))
     B = int(rng.choice([1, 3, 17, 64, 65, 70]))
@@ -70,3 +75,28 @@ def test_fuzz_plans(gpu_lib, oracle_pool, seed):
     say(info)
     out, lse = run_gpu(gpu_lib, p, chunk_keys=chunk, num_cus=cus)
     compare(p, *to_f64(out, lse), *oracle_pool.run(p), what=info)
+
+
+def _rope_supported(seed) -> bool:
+    # Query RoPE runs in the streaming kernel: bf16 caches, or fp8 with D 128.
+    _, kv_dt, D = _dtypes(seed, np.random.default_rng(5000 + seed))
+    return kv_dt == "bf16" or (kv_dt == "e4m3" and D == 128)
+
+
+@pytest.mark.parametrize("seed", [s for s in range(80) if _rope_supported(s)])
+def test_fuzz_plans_rope(gpu_lib, oracle_pool, seed):
+    """The same seeded shapes with the queries rotated by RoPE at their tree
+    positions, for the cache dtypes RoPE serves."""
+    import torch
+
+    from workloads import rope_cos_sin, rope_positions
+
+    p, chunk, cus = _fuzz_case(seed)
+    info = (f"[plan fuzz rope {seed}] B={p.batch} Hq={p.num_qo_heads} Hkv={p.num_kv_heads} "
+            f"D={p.head_dim} ps={p.page_size} {p.kv_dtype} mask={p.info['mask_kind']}/"
+            f"{p.mask_layout} maxL={p.max_qo_len} chunk={chunk} cus={cus or 'device'}")
+    say(info)
+    cs = rope_cos_sin(rope_positions(p), p.head_dim)
+    out, lse = run_gpu(gpu_lib, p, chunk_keys=chunk, num_cus=cus,
+                       q_cos_sin=torch.from_numpy(np.ascontiguousarray(cs)).cuda())
+    compare(p, *to_f64(out, lse), *oracle_pool.run(p, q_cos_sin=cs), what=info)
