@@ -15,7 +15,7 @@ namespace vat {
 const void* tile_kernel(int kv_dtype, int head_dim, int rt);
 const void* stream_kernel(int kv_dtype, int head_dim, int rt, int dma_waves, int pair,
                           int mask_mode, int rope, int heads_per_group, int stages);
-const void* merge_kernel(int q_is_f32, int head_dim, int rows_per_workgroup);
+const void* merge_kernel(int q_is_f32, int head_dim, int rows_per_workgroup, int one_slice_request);
 const void* append_kernel(int src_dtype, int cache_dtype, int pow2_scales, int units);
 const void* append_rope_kernel(int src_dtype, int cache_dtype, int pow2_scales);
 const void* read_probe_kernel();
@@ -215,7 +215,8 @@ vat_status_t launch_merge(const vat_problem_t* p, const vat_plan_t& plan,
   a.num_ids = plan.num_chunk_ids;
   a.row_groups = (plan.rows_per_block + plan.merge_rows - 1) / plan.merge_rows;
   a.slices = plan.slices;
-  const void* fn = vat::merge_kernel(p->q_dtype == VAT_F32, p->head_dim, plan.merge_rows);
+  const void* fn = vat::merge_kernel(p->q_dtype == VAT_F32, p->head_dim, plan.merge_rows,
+                                     plan.slices > 0 && p->batch == 1);
   void* args[] = {&a};
   hipError_t e = hipLaunchKernel(fn, dim3(plan.merge_grid, 1, 1), dim3(plan.merge_threads, 1, 1),
                                  args, 0, stream);

@@ -20,7 +20,13 @@ namespace vat {
 // group share each address), so the weights need no cross-lane traffic; a
 // row with more partials than one round holds takes several rounds, combined
 // with a running max that rescales what came before.
-template <int QF32, int D, bool SPLIT>
+//
+// PRE (one request over balanced slices): the request's pages start at index
+// 0, so its partials are slots 0 .. n - 1 whatever the page table holds. The
+// first round of their loads is issued before the request-table reads, and
+// what lies at or past n is dropped once those land: one dependent round of
+// loads instead of two.
+template <int QF32, int D, bool SPLIT, bool PRE = false>
 __global__ __launch_bounds__(kMergeThreads) void vat_merge(MergeArgs a) {
   constexpr int PER = D / 16;  // head dims per lane: 8 or 4
   constexpr int U = 64 / PER;  // partials per lane per round: 8 or 16
@@ -35,6 +41,25 @@ __global__ __launch_bounds__(kMergeThreads) void vat_merge(MergeArgs a) {
   x /= a.row_blocks;
   const int h = x % a.hkv;
   const int b = x / a.hkv;
+  float pre_ls[U];
+  f32x4 pre_v[U][PER / 4];
+  if constexpr (PRE) {
+    const int plocal = rg * ROWS + (SPLIT ? (int)(threadIdx.x >> 6) : (int)(threadIdx.x >> 4));
+    const int pph = SPLIT ? sub : 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = pph + u * STEP;
+      pre_ls[u] = kNegInf;
+      if (i < a.slices && plocal < a.rows_per_block) {
+        const long long sl =
+            (((long long)i * a.hkv + h) * a.row_blocks + rb) * a.rows_per_block + plocal;
+        pre_ls[u] = a.part_lse[sl];
+        const f32x4* po = (const f32x4*)(a.part_o + sl * D + l16 * PER);
+#pragma unroll
+        for (int k = 0; k < PER / 4; ++k) pre_v[u][k] = po[k];
+      }
+    }
+  }
   const Req r = make_req(a.kv_indptr[b], a.kv_indptr[b + 1], a.last_page_len[b], a.qo_indptr[b],
                          a.qo_indptr[b + 1], 0, a.page_shift, a.num_kv_indices, a.tokens);
   int n, first;  // partials of request b: slots first + i, i < n
@@ -71,6 +96,16 @@ __global__ __launch_bounds__(kMergeThreads) void vat_merge(MergeArgs a) {
     for (int u = 0; u < U; ++u) {
       const int i = i0 + ph + u * STEP;
       ls[u] = kNegInf;
+      if constexpr (PRE) {
+        if (i0 == 0 && first == 0) {  // the round loaded ahead (slot i, i < n <= slices)
+          if (i < n && ok) {
+            ls[u] = pre_ls[u];
+#pragma unroll
+            for (int k = 0; k < PER / 4; ++k) v[u][k] = pre_v[u][k];
+          }
+          continue;
+        }
+      }
       if (i < n && ok) {
         const long long sl = slot(i);
         ls[u] = a.part_lse[sl];
@@ -138,14 +173,23 @@ __global__ __launch_bounds__(kMergeThreads) void vat_merge(MergeArgs a) {
   if (l16 == 0) a.lse[orow] = den > 0.f ? (m + fast_log2(den)) * kLn2 : kNegInf;
 }
 
-// rows_per_workgroup: kMergeRows (one row per wave, SPLIT) or kMergeRows4.
-const void* merge_kernel(int q_is_f32, int head_dim, int rows_per_workgroup) {
+template <bool PRE>
+const void* merge_variant(int q_is_f32, int head_dim, int rows_per_workgroup) {
   if (rows_per_workgroup == kMergeRows4) {
-    if (q_is_f32) return (const void*)(head_dim == 64 ? vat_merge<1, 64, false> : vat_merge<1, 128, false>);
-    return (const void*)(head_dim == 64 ? vat_merge<0, 64, false> : vat_merge<0, 128, false>);
+    if (q_is_f32)
+      return (const void*)(head_dim == 64 ? vat_merge<1, 64, false, PRE> : vat_merge<1, 128, false, PRE>);
+    return (const void*)(head_dim == 64 ? vat_merge<0, 64, false, PRE> : vat_merge<0, 128, false, PRE>);
   }
-  if (q_is_f32) return (const void*)(head_dim == 64 ? vat_merge<1, 64, true> : vat_merge<1, 128, true>);
-  return (const void*)(head_dim == 64 ? vat_merge<0, 64, true> : vat_merge<0, 128, true>);
+  if (q_is_f32)
+    return (const void*)(head_dim == 64 ? vat_merge<1, 64, true, PRE> : vat_merge<1, 128, true, PRE>);
+  return (const void*)(head_dim == 64 ? vat_merge<0, 64, true, PRE> : vat_merge<0, 128, true, PRE>);
+}
+
+// rows_per_workgroup: kMergeRows (one row per wave, SPLIT) or kMergeRows4;
+// one_slice_request: balanced slices with a batch of one request (PRE).
+const void* merge_kernel(int q_is_f32, int head_dim, int rows_per_workgroup, int one_slice_request) {
+  return one_slice_request ? merge_variant<true>(q_is_f32, head_dim, rows_per_workgroup)
+                           : merge_variant<false>(q_is_f32, head_dim, rows_per_workgroup);
 }
 
 }  // namespace vat

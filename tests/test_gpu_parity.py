@@ -292,6 +292,15 @@ SLICE_CASES = {
                        mask_kind="causal"),
     "d64_ps4": dict(prefix_lens=[1000, 250, 3100], qo_lens=[2, 7, 4], num_qo_heads=8, num_kv_heads=4,
                     head_dim=64, page_size=4, mask_kind="random", mask_density=0.5),
+    # One request (the merge loads its first round of partials ahead of the
+    # request table), with spare page-index capacity so that it covers only
+    # some of the slices, and up to 256 slices per head (several rounds).
+    "one_bf16": dict(prefix_lens=[5000], qo_lens=[9], num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                     mask_kind="tree", extra_indices=40),
+    "one_d64_ps4": dict(prefix_lens=[3000], qo_lens=[17], num_qo_heads=16, num_kv_heads=2,
+                        head_dim=64, page_size=4, extra_indices=3),
+    "one_e4m3": dict(prefix_lens=[6000], qo_lens=[5], num_qo_heads=16, num_kv_heads=4, head_dim=128,
+                     kv_dtype="e4m3", fp8_absmax_scales=True, extra_indices=7),
 }
 
 
