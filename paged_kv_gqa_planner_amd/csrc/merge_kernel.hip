@@ -35,6 +35,13 @@ __global__ __launch_bounds__(kMergeThreads) void vat_merge(MergeArgs a) {
   const int lane = threadIdx.x & 63;
   const int sub = lane >> 4, l16 = lane & 15;
   int x = blockIdx.x;
+  // The pointer line of the argument block joins the opening round of
+  // argument loads (the block index below waits on it), instead of arriving
+  // in a second round after the index arithmetic.
+  {
+    const void* p0 = a.part_o;
+    asm volatile("" : "+s"(x) : "s"(p0));
+  }
   const int rg = x % a.row_groups;
   x /= a.row_groups;
   const int rb = x % a.row_blocks;

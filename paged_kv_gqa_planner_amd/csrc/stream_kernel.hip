@@ -791,6 +791,15 @@ __device__ __forceinline__ void merge_pair_state(StreamAcc<D, RT>& acc, float (&
 template <int KV, int D, int RT, int NS, int DW, int P, int SK, bool ROWS, bool ROPE, int HP = 1>
 __global__ __launch_bounds__(kStreamThreads, 1) void vat_stream(PartialArgs a) {
   using G = StreamGeom<KV, D, DW, SK, HP>;
+  // The argument block spans three 64-byte lines. Needing the first one
+  // (the pointers) here puts it in the opening round of argument loads; left
+  // alone, the compiler fetches it only after the block-index arithmetic, a
+  // second dependent round of about half a microsecond before any request
+  // table load can start.
+  {
+    const void* p0 = a.q;
+    asm volatile("" ::"s"(p0));
+  }
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   int* win = (int*)(smem + NS * G::STAGE);
   const int lane = threadIdx.x & 63;
