@@ -30,10 +30,15 @@ def _call(lib, p, t, fn):
 def test_noalloc_matches_verify_attention_twice_larger_then_smaller(gpu_lib):
     # First the fp8 batch-64 workload (a 12 MiB workspace), then a smaller
     # masked bf16 tree batch (a few hundred KiB): the second call reuses the
-    # array that still holds the first call's partials.
+    # array that still holds the first call's partials. Then one request over
+    # balanced slices, whose merge loads slots ahead of the request table:
+    # the slots past its own hold the earlier calls' partials and must be
+    # dropped.
     cases = [make_config(5),
              make_case(41, prefix_lens=[300, 45, 900], qo_lens=[9, 4, 13], num_qo_heads=8,
-                       num_kv_heads=2, head_dim=128, page_size=16, mask_kind="tree")]
+                       num_kv_heads=2, head_dim=128, page_size=16, mask_kind="tree"),
+             make_case(43, prefix_lens=[2500], qo_lens=[9], num_qo_heads=16, num_kv_heads=4,
+                       head_dim=128, page_size=16, mask_kind="tree", extra_indices=5)]
     sizes = []
     for i, p in enumerate(cases):
         t = to_device(p)
@@ -48,7 +53,7 @@ def test_noalloc_matches_verify_attention_twice_larger_then_smaller(gpu_lib):
         assert torch.equal(got_o.view(torch.int16), ref_o.view(torch.int16))
         assert torch.equal(got_l, ref_l)
         compare(p, *to_f64(got_o, got_l), *oracle_of(p), what=f"noalloc call {i}")
-    assert sizes[1] < sizes[0]
+    assert sizes[1] < sizes[0] and sizes[2] < sizes[0]
 
 
 def test_noalloc_refuses_a_workspace_beyond_the_array(gpu_lib):
