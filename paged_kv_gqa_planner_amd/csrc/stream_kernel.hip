@@ -676,6 +676,21 @@ struct RowSet {
 // compiler cannot hoist the lane-dependent part of these addresses out of
 // the stage loop (where, in the two-tile two-pass variant, the hoisted
 // values would not fit the registers and spill).
+// Raw buffer resources (gfx9 family): word 3 of the descriptor for plain
+// byte-addressed 32-bit data, with the hardware dropping out-of-range
+// stores; the cache-policy operand's SC1 bit asks for device scope.
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kCachePolicySC1 = 16;
+
+// A pointer the compiler can keep in scalar registers (buffer descriptors
+// must be); the caller guarantees it is the same in every lane.
+__device__ __forceinline__ void* wave_uniform(const void* p) {
+  const unsigned long long v = (unsigned long long)p;
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)v);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(v >> 32));
+  return (void*)(((unsigned long long)hi << 32) | lo);
+}
+
 template <int D, int RT, bool OPAQUE = false>
 __device__ __forceinline__ void write_rows(const StreamAcc<D, RT>& acc, const float (&lrow)[RT],
                                            const PartialArgs& a, int q_start, int L, int rbase,
@@ -684,6 +699,16 @@ __device__ __forceinline__ void write_rows(const StreamAcc<D, RT>& acc, const fl
   if constexpr (OPAQUE) asm volatile("" : "+v"(lane));
   const int l16 = lane & 15, j4 = lane >> 4;
   const long long pid = ((long long)slot * a.hkv + h) * a.row_blocks + rb;
+  // Partials go out as device-scope buffer stores (cache policy SC1): written
+  // through this XCD's L2 to the memory side, where the merge kernel reads
+  // them, instead of staying dirty in L2 until the kernel's end flushes it.
+  // Buffer bases must be wave-uniform; the segment's row block is.
+  const __amdgpu_buffer_rsrc_t rpo = __builtin_amdgcn_make_buffer_rsrc(
+      wave_uniform(a.part_o + pid * a.rows_per_block * D), 0,
+      __builtin_amdgcn_readfirstlane(a.rows_per_block * D * 4), kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rpl = __builtin_amdgcn_make_buffer_rsrc(
+      wave_uniform(a.part_lse + pid * a.rows_per_block), 0,
+      __builtin_amdgcn_readfirstlane(a.rows_per_block * 4), kRawBufferWord3);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const float lsum = lrow[rt];
@@ -703,10 +728,13 @@ __device__ __forceinline__ void write_rows(const StreamAcc<D, RT>& acc, const fl
       }
       if (j4 == 0) a.lse[orow] = lsum > 0.f ? lse2 * kLn2 : kNegInf;
     } else {
-      float* op = a.part_o + (pid * a.rows_per_block + local) * D;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) *(f32x4*)(op + 16 * dt + 4 * j4) = acc.o[rt][dt] * inv;
-      if (j4 == 0) a.part_lse[pid * a.rows_per_block + local] = lse2;
+      for (int dt = 0; dt < NDT; ++dt)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc.o[rt][dt] * inv), rpo,
+                                               (local * D + 16 * dt + 4 * j4) * 4, 0, kCachePolicySC1);
+      if (j4 == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse2), rpl, local * 4, 0,
+                                              kCachePolicySC1);
     }
   }
 }
