@@ -182,16 +182,10 @@ vat_status_t make_plan(const vat_problem_t* p, int32_t num_cus, vat_plan_t* plan
     // Up to six computing waves leave the last four (or two) to issue the DMA
     // alone, so a computing wave never stalls behind the memory queue.
     dw = wr * wk <= 4 ? 4 : (rt == 1 && wr * wk <= 6 ? 2 : kStreamThreads / 64);
-    // One row tile of bf16 D = 128 keys (decode): a single computing wave
-    // takes every 64-key stage whole and all eight waves issue the loads --
-    // no pair hand-off, twice the DMA issuers (measured on the B64 decode
-    // workload: 224.5 -> 215.3 us per launch). Not with query RoPE, whose
-    // second QK product per tile makes that one wave the bottleneck
-    // (224.7 -> 247.5 us).
-    if (bt == 1 && p->kv_dtype == VAT_BF16 && D == 128 && !p->rope) {
-      wk = 1;
-      dw = kStreamThreads / 64;
-    }
+    // One row tile (decode) keeps this pair too. A single computing wave
+    // with all eight waves issuing was faster while the K/V loads kept the
+    // default cache policy (B64 decode 224.5 -> 215.3 us); with non-temporal
+    // loads the pair with four DMA waves is (210-214 -> 194-195 us).
   } else if (tiles <= 3) {
     rt = int(tiles);
     wr = 1;
